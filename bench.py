@@ -1,0 +1,236 @@
+"""Benchmark of the vision-encoder self-attention forward (libvitattn) on one GPU.
+
+A step is one pass of the attention forward over every layer of the workload
+(fresh, seeded inputs per layer, all resident in HBM before timing starts):
+for the default workload, SigLIP-So400m/14 at 224 px with two views
+(B=2, N=256, H=16, D=72, packed QKV), that is 27 back-to-back layer calls.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+Prints ONE JSON line.  `value` is TFLOP/s over the timed steps (algorithmic
+flops 4*B*H*N^2*D per layer call).  Also reported: us per layer call, the
+roofline of the kernel (per-launch HIP-event timing on the launch stream),
+the fp64 CPU oracle timed on this host as a baseline, parity of the timed
+outputs with that oracle, and the same figures for the 384 px SigLIP
+workload (B=48, N=729), where the kernel is compute-bound.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, vendor figure
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, vendor figure
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)   # flop per byte
+
+
+def _parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c3")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-target", action="store_true",
+                   help="skip the 384 px SigLIP (B=48, N=729) figures")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU time budget for the oracle baseline")
+    return p.parse_args()
+
+
+def _device_inputs(wl, device, layers):
+    import numpy as np
+    import torch
+    from workloads import make_layer
+
+    ins, outs, host = [], [], []
+    for layer in range(layers):
+        li = make_layer(wl, layer)
+        arrs = li.in_layout(wl.layout)
+        ts = [torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+              if a is not None else None for a in arrs]
+        ins.append(ts)
+        B, N, H, D = wl.B, wl.N, wl.H, wl.D
+        shape = (B, N, H, D) if wl.layout == 1 else (B, H, N, D)
+        outs.append(torch.empty(shape, dtype=torch.bfloat16, device=device))
+        host.append(arrs)
+    return ins, outs, host
+
+
+def _roofline(wl, launch_s):
+    ai = wl.flops_per_layer / wl.bytes_per_layer
+    if ai >= RIDGE:
+        ach = wl.flops_per_layer / launch_s / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+    ach = wl.bytes_per_layer / launch_s / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBPS, "traffic": None}
+
+
+def _time_steps(va, wl, ins, outs, steps, warmup, stream):
+    """Warmup, then exactly `steps` timed steps; per-launch events as well."""
+    import torch
+
+    def step(evs=None):
+        for i, (ts, o) in enumerate(zip(ins, outs)):
+            if evs is not None:
+                evs[2 * i].record(stream)
+            va.fwd(ts[0], ts[1], ts[2], out=o, scale=wl.scale, stream=stream)
+            if evs is not None:
+                evs[2 * i + 1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    L = len(ins)
+    launch_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+                  for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(steps):
+        step(launch_evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in launch_evs for i in range(L)]
+    return total_ms, launch_ms, wall
+
+
+def _cpu_baseline(wl, host, budget_s):
+    """Times the fp64 oracle on this host: one full step (every layer, which
+    also gives the parity reference), then more layer calls until the time
+    budget is spent."""
+    import oracle
+
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    oracle.set_threads(threads)
+    refs = []
+    t0 = time.perf_counter()
+    for arrs in host:
+        refs.append(oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale))
+    done = len(host)
+    while time.perf_counter() - t0 < budget_s:
+        arrs = host[done % len(host)]
+        oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale)
+        done += 1
+    dt = time.perf_counter() - t0
+    tflops = wl.flops_per_layer * done / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{done} layer calls of the timed workload ({done / len(host):.2f} steps) "
+                      f"in {dt:.1f} s, fp64, C + OpenMP",
+            "ms_per_layer": dt / done * 1e3}, refs
+
+
+def _parity(wl, outs_dev, refs):
+    import numpy as np
+    mx, tot, cnt = 0.0, 0.0, 0
+    for o, ref in zip(outs_dev, refs):
+        got = o.float().cpu().numpy().astype(np.float64)
+        if wl.layout == 0:
+            got = got.transpose(0, 2, 1, 3)
+        err = np.abs(got - ref)
+        mx = max(mx, float(err.max()))
+        tot += float(err.sum())
+        cnt += err.size
+    mean = tot / cnt
+    return {"max_abs": mx, "mean_abs": mean, "pass": bool(mx <= 2e-2 and mean <= 2e-3),
+            "layers": len(refs)}
+
+
+def _trimmed_median(xs):
+    xs = sorted(xs)
+    k = int(len(xs) * 0.05)
+    xs = xs[k:len(xs) - k] if len(xs) > 2 * k else xs
+    return xs[len(xs) // 2]
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
+              "forward shards over images with no communication, so the single-GPU "
+              "throughput is the per-GPU figure", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import vit_self_attention_amd as va
+    from workloads import WORKLOADS
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    stream = torch.cuda.current_stream(device)
+    wl = WORKLOADS[args.workload]
+
+    ins, outs, host = _device_inputs(wl, device, wl.layers)
+    total_ms, launch_ms, wall = _time_steps(va, wl, ins, outs, args.steps, args.warmup, stream)
+    ms_per_step = total_ms / args.steps
+    value = wl.flops_per_layer * wl.layers / (ms_per_step * 1e-3) / 1e12
+    mean_launch_s = sum(launch_ms) / len(launch_ms) * 1e-3
+    roof = _roofline(wl, mean_launch_s)
+
+    result = {
+        "metric": "vision-attn fwd TFLOP/s & us/layer (SigLIP N=256,H=16,D=72,B=2); % MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64, bf16 RNE)",
+        "config": {"workload": wl.name, "B": wl.B, "N": wl.N, "H": wl.H, "D": wl.D,
+                   "layout": "packed [B,N,3,H,D]" if wl.layout == 1 else "separate [B,H,N,D]",
+                   "layers_per_step": wl.layers, "scale": wl.scale},
+        "us_per_layer": ms_per_step * 1e3 / wl.layers,
+        "us_per_launch_kernel": mean_launch_s * 1e6,
+        "mfma_frac": value / PEAK_BF16_TFLOPS,
+        "hbm_gbps": wl.bytes_per_layer * wl.layers / (ms_per_step * 1e-3) / 1e9,
+        "roofline": roof,
+        "wall_s_timed": wall,
+    }
+
+    if not args.no_cpu_baseline:
+        cpu, refs = _cpu_baseline(wl, host, args.cpu_seconds)
+        result["cpu_baseline"] = cpu
+        result["parity"] = _parity(wl, outs, refs)
+    else:
+        result["cpu_baseline"] = None
+
+    if not args.no_target and wl.key != "c5":
+        t = WORKLOADS["c5"]
+        tins, touts, _ = _device_inputs(t, device, 1)
+        samples = []
+        for _ in range(3):
+            _time_steps(va, t, tins, touts, 1, 1, stream)
+        for _ in range(50):
+            tot, lm, _ = _time_steps(va, t, tins, touts, 1, 0, stream)
+            samples.append(lm[0])
+        us = _trimmed_median(samples) * 1e3
+        tf = t.flops_per_layer / (us * 1e-6) / 1e12
+        result["siglip384_target"] = {
+            "workload": t.name, "us_per_layer": us, "tflops": tf,
+            "mfma_frac": tf / PEAK_BF16_TFLOPS, "target_frac": 0.40,
+            "hbm_gbps": t.bytes_per_layer / (us * 1e-6) / 1e9,
+            "roofline": _roofline(t, us * 1e-6),
+            "timing": "per-launch HIP events, median of 50 after 5% trim"}
+        del tins, touts
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,99 @@
+/*
+ * libvitattn -- forward pass of the bidirectional multi-head self-attention
+ * of a ViT / SigLIP vision encoder on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every image b < B and head h < H, with Q, K, V the
+ * N x D bf16 matrices of that (image, head) over the N patch tokens:
+ *
+ *     O = softmax(scale * Q K^T) V          (softmax along the key axis)
+ *
+ * This is the attention core that the Pi0 Flash Attention tutorial
+ * ("Pi0 VLA deployment: accelerating the vision encoder with Flash
+ * Attention", section 1) names as the dominant cost of the vision encoder,
+ * and that its section 3.2 swaps for a fused kernel fed by the block's fused
+ * qkv projection, with inputs and outputs unchanged.  Every token attends to
+ * every token (no mask); no dropout (inference).
+ *
+ * Numerics: bf16 inputs, fp32 accumulation and softmax state, probabilities
+ * rounded to bf16 for the P V product, bf16 output rounded to nearest even.
+ * Results are deterministic: the same inputs give the same output bits.
+ *
+ * C ABI only: plain pointers and sizes.  The library allocates no device
+ * memory, keeps no state between calls and may be called from several host
+ * threads at once.
+ */
+#ifndef VITATTN_H
+#define VITATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input layouts. */
+enum {
+  /* q, k, v: three separate bf16 tensors, each [B][H][N][D] (row-major).
+   * out: [B][H][N][D]. */
+  VITATTN_LAYOUT_SEPARATE_BHND = 0,
+  /* qkv_or_q: the fused qkv activation [B][N][3][H][D] (slot 0 = Q,
+   * 1 = K, 2 = V), i.e. the [B, N, 3*H*D] output of the qkv projection;
+   * k and v must be NULL.  out: [B][N][H][D], i.e. [B, N, H*D], the input
+   * of the output projection. */
+  VITATTN_LAYOUT_PACKED_BN3HD = 1
+};
+
+/* Status codes (0 = success; negative = error, nothing launched). */
+enum {
+  VITATTN_OK = 0,
+  VITATTN_ERR_NULL_POINTER = -1,     /* a required pointer is NULL */
+  VITATTN_ERR_BAD_SIZE = -2,         /* B, H or N negative */
+  VITATTN_ERR_UNSUPPORTED_D = -3,    /* D is not 64 or 72 */
+  VITATTN_ERR_BAD_SCALE = -4,        /* scale is NaN or infinite */
+  VITATTN_ERR_BAD_LAYOUT = -5,       /* unknown layout, or k/v given with the packed layout */
+  VITATTN_ERR_MISALIGNED = -6,       /* a pointer is not 16-byte aligned */
+  VITATTN_ERR_TOO_LARGE = -7,        /* the problem exceeds the launch limits */
+  VITATTN_ERR_LAUNCH = -8,           /* the HIP launch reported an error */
+  VITATTN_ERR_OVERLAP = -9           /* out overlaps an input buffer */
+};
+
+/*
+ * vitattn_fwd -- O = softmax(scale * Q K^T) V for all B*H (image, head) pairs.
+ *
+ *   qkv_or_q  device pointer, bf16.  Separate layout: Q [B][H][N][D].
+ *             Packed layout: the fused qkv buffer [B][N][3][H][D].
+ *   k, v      device pointers, bf16 [B][H][N][D] for the separate layout;
+ *             must be NULL for the packed layout.
+ *   out       device pointer, bf16, written in full: [B][H][N][D] (separate)
+ *             or [B][N][H][D] (packed).  Must not overlap any input.
+ *   B, H, N   images, heads, tokens.  Any N >= 1 (not only tile multiples);
+ *             B, H or N equal to 0 is an empty problem: returns VITATTN_OK
+ *             and launches nothing (its pointers may then be NULL).
+ *   D         head dimension: 64 or 72.
+ *   scale     logit scale, any finite value (usually 1/sqrt(D)); 0 gives
+ *             uniform attention.
+ *   layout    VITATTN_LAYOUT_SEPARATE_BHND or VITATTN_LAYOUT_PACKED_BN3HD.
+ *   stream    a hipStream_t (NULL = the null stream).  The call only
+ *             enqueues one kernel on it and returns without waiting.
+ *
+ * Ownership: the caller owns every buffer and keeps it alive until the
+ * enqueued work has finished.  All pointers must be 16-byte aligned.
+ *
+ * Errors: every argument is checked on the host before anything is
+ * launched, and a failed check returns its negative code with no device
+ * work.  VITATTN_ERR_LAUNCH means the runtime rejected the launch (for
+ * instance, no gfx950 device is current).  Faults inside the kernel are
+ * reported, as for any HIP kernel, by the next synchronising HIP call.
+ */
+int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, void* out, int B, int H,
+                int N, int D, float scale, int layout, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* vitattn_strerror(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int vitattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VITATTN_H */

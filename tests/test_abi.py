@@ -1,0 +1,148 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/vitattn.h declares, and rejects bad arguments on the host before any
+device call.  No call here reaches a kernel launch: every argument set is
+either invalid or an empty problem, both of which return before HIP is used.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vitattn.h")
+
+A = 0x7f0000000000  # fake, 16-byte aligned "device" addresses: never dereferenced
+OUT = 0x7f1000000000
+
+
+@pytest.fixture(scope="module")
+def va():
+    import vit_self_attention_amd
+    return vit_self_attention_amd
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vitattn_[a-z_]+)\s*\(", text)))
+
+
+def _declared_enums():
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(VITATTN_\w+)\s*=\s*(-?\d+)", text)}
+
+
+def test_exports_every_declared_function(va):
+    declared = _declared_functions()
+    assert declared == sorted(va.EXPORTED)
+    lib = ctypes.CDLL(va.LIBRARY)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header(va):
+    enums = _declared_enums()
+    for name, value in enums.items():
+        if name.startswith("VITATTN_ERR_") or name == "VITATTN_OK":
+            assert getattr(va._binding, name[len("VITATTN_"):]) == value, name
+    assert enums["VITATTN_LAYOUT_SEPARATE_BHND"] == va.LAYOUT_SEPARATE
+    assert enums["VITATTN_LAYOUT_PACKED_BN3HD"] == va.LAYOUT_PACKED
+
+
+def test_version_and_strerror(va):
+    assert va.version() == 100
+    for name, code in _declared_enums().items():
+        if name.startswith("VITATTN_ERR_"):
+            msg = va.strerror(code)
+            assert msg and msg != "unknown status"
+    assert va.strerror(12345) == "unknown status"
+    assert va.strerror(0) == "success"
+
+
+def _call(va, q=A, k=None, v=None, out=OUT, B=2, H=3, N=197, D=64, scale=0.125,
+          layout=None):
+    if layout is None:
+        layout = va.LAYOUT_PACKED if k is None else va.LAYOUT_SEPARATE
+    return va.fwd_raw(q, k, v, out, B, H, N, D, scale, layout, None)
+
+
+@pytest.mark.parametrize("D", [0, 1, 32, 63, 65, 71, 80, 96, 128, -64])
+def test_unsupported_head_dim(va, D):
+    assert _call(va, D=D) == va._binding.ERR_UNSUPPORTED_D
+
+
+@pytest.mark.parametrize("bhn", [(-1, 1, 1), (1, -1, 1), (1, 1, -1)])
+def test_negative_sizes(va, bhn):
+    B, H, N = bhn
+    assert _call(va, B=B, H=H, N=N) == va._binding.ERR_BAD_SIZE
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+def test_non_finite_scale(va, scale):
+    assert _call(va, scale=scale) == va._binding.ERR_BAD_SCALE
+
+
+def test_null_pointers(va):
+    e = va._binding.ERR_NULL_POINTER
+    assert _call(va, q=0) == e
+    assert _call(va, out=0) == e
+    sep = va.LAYOUT_SEPARATE
+    assert _call(va, k=A + 4096, v=None, layout=sep) == e
+    assert _call(va, k=None, v=A + 4096, layout=sep) == e
+
+
+def test_bad_layout(va):
+    e = va._binding.ERR_BAD_LAYOUT
+    assert _call(va, layout=2) == e
+    assert _call(va, layout=-1) == e
+    # k / v must be NULL with the packed layout
+    assert _call(va, k=A + 2 ** 30, v=A + 2 ** 31, layout=va.LAYOUT_PACKED) == e
+
+
+def test_misaligned(va):
+    e = va._binding.ERR_MISALIGNED
+    assert _call(va, q=A + 2) == e
+    assert _call(va, out=OUT + 8) == e
+    sep = va.LAYOUT_SEPARATE
+    assert _call(va, k=A + 2 ** 30 + 4, v=A + 2 ** 31) == e
+    assert _call(va, k=A + 2 ** 30, v=A + 2 ** 31 + 2, layout=sep) == e
+
+
+def test_overlap(va):
+    e = va._binding.ERR_OVERLAP
+    B, H, N, D = 2, 3, 197, 64
+    t_bytes = B * H * N * D * 2
+    # packed: out inside the qkv buffer (3 * t_bytes long)
+    assert _call(va, out=A + 2 * t_bytes, B=B, H=H, N=N, D=D) == e
+    assert _call(va, out=A - t_bytes + 16, B=B, H=H, N=N, D=D) == e
+    # separate: out overlapping v
+    kk, vv = A + 2 ** 30, A + 2 ** 31
+    assert _call(va, k=kk, v=vv, out=vv + 1024, B=B, H=H, N=N, D=D) == e
+
+
+def test_too_large(va):
+    assert _call(va, B=2 ** 30, H=2 ** 10, N=2 ** 10) == va._binding.ERR_TOO_LARGE
+
+
+@pytest.mark.parametrize("bhn", [(0, 3, 7), (2, 0, 7), (2, 3, 0), (0, 0, 0)])
+def test_empty_problem_is_a_noop(va, bhn):
+    """Empty problems return success without touching the device (the
+    addresses passed here are not valid device memory)."""
+    B, H, N = bhn
+    assert _call(va, B=B, H=H, N=N) == va.OK
+    assert _call(va, k=A + 2 ** 30, v=A + 2 ** 31, B=B, H=H, N=N) == va.OK
+    # a zero-element tensor has no storage: NULL pointers are accepted then
+    assert _call(va, q=0, out=0, B=B, H=H, N=N) == va.OK
+    # but the other arguments are still checked
+    assert _call(va, q=0, out=0, B=B, H=H, N=N, D=80) == va._binding.ERR_UNSUPPORTED_D
+
+
+def test_python_wrapper_rejects_cpu_tensors(va):
+    import torch
+    x = torch.zeros(1, 4, 3, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        va.fwd(x)

@@ -1,0 +1,109 @@
+// C-ABI entry points of libvitattn: argument validation on the host, then
+// one kernel launch.  Every check here runs before any HIP call, so a bad
+// argument never reaches the device.
+#include "vitattn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "vitattn_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000 * 0 + 100 * 1 + 0;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(b_bytes) && b0 < a0 + static_cast<uintptr_t>(a_bytes);
+}
+
+}  // namespace
+
+extern "C" int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, void* out,
+                           int B, int H, int N, int D, float scale, int layout, void* stream) {
+  if (layout != VITATTN_LAYOUT_SEPARATE_BHND && layout != VITATTN_LAYOUT_PACKED_BN3HD)
+    return VITATTN_ERR_BAD_LAYOUT;
+  if (layout == VITATTN_LAYOUT_PACKED_BN3HD && (k != nullptr || v != nullptr))
+    return VITATTN_ERR_BAD_LAYOUT;
+  if (B < 0 || H < 0 || N < 0) return VITATTN_ERR_BAD_SIZE;
+  if (D != 64 && D != 72) return VITATTN_ERR_UNSUPPORTED_D;
+  if (!isfinite(scale)) return VITATTN_ERR_BAD_SCALE;
+  // An empty problem has nothing to read or write; its buffers may be NULL
+  // (a zero-element tensor usually has no storage).
+  if (B == 0 || H == 0 || N == 0) return VITATTN_OK;
+  if (!qkv_or_q || !out) return VITATTN_ERR_NULL_POINTER;
+  if (layout == VITATTN_LAYOUT_SEPARATE_BHND && (!k || !v)) return VITATTN_ERR_NULL_POINTER;
+  if (!aligned16(qkv_or_q) || !aligned16(out)) return VITATTN_ERR_MISALIGNED;
+  if (layout == VITATTN_LAYOUT_SEPARATE_BHND && (!aligned16(k) || !aligned16(v)))
+    return VITATTN_ERR_MISALIGNED;
+
+  // Problem-size limits: element offsets are 64-bit inside the kernel; the
+  // grid is one workgroup per (image, head, query block) and must fit int32.
+  const int64_t rows = static_cast<int64_t>(B) * H * N;  // (b, h, token) rows
+  if (rows > (int64_t(1) << 40)) return VITATTN_ERR_TOO_LARGE;
+  const int64_t pairs = static_cast<int64_t>(B) * H;
+  if (pairs * ((static_cast<int64_t>(N) + 31) / 32) > (int64_t(1) << 30))
+    return VITATTN_ERR_TOO_LARGE;
+
+  const int64_t t_bytes = rows * D * 2;  // one of Q, K, V or O, in bytes
+  if (layout == VITATTN_LAYOUT_PACKED_BN3HD) {
+    if (overlaps(out, t_bytes, qkv_or_q, 3 * t_bytes)) return VITATTN_ERR_OVERLAP;
+  } else {
+    if (overlaps(out, t_bytes, qkv_or_q, t_bytes) || overlaps(out, t_bytes, k, t_bytes) ||
+        overlaps(out, t_bytes, v, t_bytes))
+      return VITATTN_ERR_OVERLAP;
+  }
+
+  vitattn::FwdArgs a{};
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.D = D;
+  a.scale = scale;
+  a.o = static_cast<uint16_t*>(out);
+  const int64_t hd = static_cast<int64_t>(H) * D;
+  if (layout == VITATTN_LAYOUT_PACKED_BN3HD) {
+    const uint16_t* base = static_cast<const uint16_t*>(qkv_or_q);
+    a.q = base;
+    a.k = base + hd;
+    a.v = base + 2 * hd;
+    const int64_t st = 3 * hd, sb = static_cast<int64_t>(N) * st;
+    a.q_sb = a.k_sb = a.v_sb = sb;
+    a.q_sh = a.k_sh = a.v_sh = D;
+    a.q_st = a.k_st = a.v_st = st;
+    a.o_sb = static_cast<int64_t>(N) * hd;
+    a.o_sh = D;
+    a.o_st = hd;
+  } else {
+    a.q = static_cast<const uint16_t*>(qkv_or_q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    const int64_t sh = static_cast<int64_t>(N) * D, sb = static_cast<int64_t>(H) * sh;
+    a.q_sb = a.k_sb = a.v_sb = a.o_sb = sb;
+    a.q_sh = a.k_sh = a.v_sh = a.o_sh = sh;
+    a.q_st = a.k_st = a.v_st = a.o_st = D;
+  }
+  return vitattn::launch_fwd(a, stream);
+}
+
+extern "C" const char* vitattn_strerror(int status) {
+  switch (status) {
+    case VITATTN_OK: return "success";
+    case VITATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case VITATTN_ERR_BAD_SIZE: return "B, H or N is negative";
+    case VITATTN_ERR_UNSUPPORTED_D: return "head dimension D must be 64 or 72";
+    case VITATTN_ERR_BAD_SCALE: return "scale must be finite";
+    case VITATTN_ERR_BAD_LAYOUT:
+      return "unknown layout, or k/v passed with the packed layout";
+    case VITATTN_ERR_MISALIGNED: return "device pointers must be 16-byte aligned";
+    case VITATTN_ERR_TOO_LARGE: return "problem exceeds the launch limits";
+    case VITATTN_ERR_LAUNCH: return "kernel launch failed";
+    case VITATTN_ERR_OVERLAP: return "out overlaps an input buffer";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int vitattn_version(void) { return kVersion; }

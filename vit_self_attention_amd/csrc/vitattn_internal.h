@@ -1,0 +1,33 @@
+// Internal interface between the C-ABI entry points (vitattn_api.cpp) and
+// the gfx950 kernels (vitattn_fwd.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace vitattn {
+
+// Per-launch description of one attention problem.  Strides are in bf16
+// elements.  For (image b, head h, token n) the row of Q starts at
+// q + b*q_sb + h*q_sh + n*q_st, and likewise for k, v and out.
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int64_t v_sb, v_sh, v_st;
+  int64_t o_sb, o_sh, o_st;
+  int B, H, N, D;
+  float scale;
+};
+
+// Enqueues the forward kernel on `stream` (a hipStream_t).  Arguments are
+// already validated.  Returns 0 or a negative VITATTN_ERR_* code.
+int launch_fwd(const FwdArgs& a, void* stream);
+
+// Number of waves per workgroup the launcher picks for a problem (1, 2 or 4);
+// exposed for tests and the benchmark's reporting.
+int pick_waves(int B, int H, int N);
+
+}  // namespace vitattn
