@@ -11,24 +11,31 @@
 // Work decomposition
 //   * one workgroup per (image, head, block of 32*NW queries); NW waves of
 //     64 lanes, each wave owning 32 queries;
-//   * keys in tiles of 64, loaded cooperatively from HBM with 128-bit loads
-//     and double-buffered in LDS: K row-major, V transposed (V^T) so both
-//     matrix products read their operands with contiguous LDS loads;
+//   * keys in tiles of 64, loaded cooperatively with 128-bit global loads
+//     and stored row-major in LDS (K two tiles ahead, V one tile ahead of
+//     the tile being reduced, each double-buffered, one barrier per tile);
 //   * both products on bf16 MFMA with fp32 accumulation, in transposed form:
-//       S^T = K Q^T       (v_mfma_f32_32x32x16_bf16; D = 72 adds one 32x32x8)
+//       S^T = K Q^T       (v_mfma_f32_32x32x16_bf16; D = 72 adds a 32x32x8)
 //       O^T += V^T P^T    (v_mfma_f32_32x32x16_bf16)
 //     With S^T in the accumulator layout, lane l holds 16 keys of query
-//     (l mod 32) per 32x32 block: the row max and row sum are mostly
-//     in-lane, and the accumulator registers are, after conversion to bf16,
-//     exactly the B operand of the second product (keys permuted within each
-//     group of 16, matched by the order in which V^T is read);
-//   * online softmax in base 2: m = running max of scale*log2(e)*s,
-//     p = exp2(scale*log2(e)*s - m), rescale by exp2(m_old - m_new);
+//     (l mod 32) per 32x32 block: the row max is mostly in-lane, and the
+//     accumulator registers, converted to bf16, are directly the B operand
+//     of the second product (keys permuted within each group of 16).  The
+//     matching V^T operand comes from row-major V through the gfx950 LDS
+//     transpose read (ds_read_b64_tr_b16), so V is never transposed in
+//     memory;
+//   * software pipeline inside each wave: the Q K^T products of tile j+1
+//     are issued while the exponentials of tile j run on the VALU, and the
+//     P V products of tile j overlap the row max of tile j+1;
+//   * online softmax in base 2 with a lazy running max: the accumulator is
+//     rescaled only when a row's max grows by more than 2^8, which keeps
+//     every probability weight <= 256;
 //   * D = 72: the P V product runs three 32-row output tiles (d 0..95); the
-//     spare row d = 72 multiplies P by a row of ones, which yields the
-//     softmax denominator from the same bf16 probabilities that weight V.
-//   * tails: keys >= N are zero-filled in LDS and masked to -inf; queries
-//     >= N are computed on zero rows and never stored.
+//     spare row d = 72 reads a column of ones stored after each V row, so
+//     the softmax denominator comes out of the same MFMA from the same bf16
+//     weights that multiply V;
+//   * tails: keys >= N are zero-filled in LDS and masked to -inf in the
+//     last tile only; queries >= N run on zero rows and are never stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,14 +47,16 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBlockN = 64;          // keys per tile
-constexpr int kKStride = 72;         // LDS row stride of the K tile (elements): 144 B
-constexpr int kVStride = kBlockN + 4;  // LDS row stride of the V^T tile (elements): 136 B
+constexpr int kBlockN = 64;           // keys per tile
+constexpr int kKStride = 72;          // K row stride in LDS (elements): 144 B
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;         // rescale only when the max grows by > 2^8
 
 struct KernelArgs {
   const uint16_t* q;
@@ -61,7 +70,7 @@ struct KernelArgs {
   int H, N;
   int qblocks;     // query blocks per (image, head)
   int grid;        // total workgroups
-  float c;         // |scale| * log2(e)
+  float c;         // max(|scale|, tiny) * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0: Q is negated instead
 };
 
@@ -73,6 +82,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   p[0] = static_cast<__bf16>(lo);
   p[1] = static_cast<__bf16>(hi);
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second.  Fed two copies of v, the two results hold, in
+// every lane, v of this lane and v of lane ^ 32 (in an order that depends on
+// the half).  The elements are copied out as integers before the bit casts:
+// a bit cast applied directly to a vector element reads element 0.
+__device__ __forceinline__ void swap_halves(float v, float& x, float& y) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  x = __builtin_bit_cast(float, r0);
+  y = __builtin_bit_cast(float, r1);
+}
+
+// max(v[lane], v[lane ^ 32])
+__device__ __forceinline__ float max_across_halves(float v) {
+  float x, y;
+  swap_halves(v, x, y);
+  return fmaxf(x, y);
+}
+
+// v[lane] + v[lane ^ 32]
+__device__ __forceinline__ float sum_across_halves(float v) {
+  float x, y;
+  swap_halves(v, x, y);
+  return x + y;
+}
+
+// v of lane (lane mod 32): the lower half's value in both halves
+__device__ __forceinline__ float lower_half_value(float v) {
+  float x, y;
+  swap_halves(v, x, y);
+  return x;
+}
+
+// LDS transpose read: within each group of 16 lanes, lane 4a+b receives
+// element b of the 8-byte rows that lanes 4j+a point at, for j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
@@ -88,13 +138,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr int kThreads = 64 * NW;
-  constexpr int kChunksPerRow = D / 8;                 // 16-byte chunks per row
-  constexpr int kChunks = kBlockN * kChunksPerRow;     // chunks per tile
-  constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
-  constexpr bool kOnesRow = (D % 32) != 0;             // spare output row carries the row sum
-  constexpr int kOutTiles = kOnesRow ? (D + 32) / 32 : D / 32;  // 3 for D=72, 2 for D=64
-  constexpr int kKTile = kBlockN * kKStride;           // elements
-  constexpr int kVTile = D * kVStride;                 // elements
+  constexpr int kCPR = D / 8;                       // 16-byte chunks per row
+  constexpr int kChunks = kBlockN * kCPR;           // chunks per tile
+  constexpr int kCPT = (kChunks + kThreads - 1) / kThreads;
+  constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
+  constexpr int kOutTiles = kOnesRow ? 3 : 2;
+  constexpr int kVStride = kOnesRow ? 80 : 72;      // V row: D values (+ [1,0,..,0] for D = 72)
+  constexpr int kKTile = kBlockN * kKStride;
+  constexpr int kVTile = kBlockN * kVStride;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKTile];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVTile];
@@ -103,7 +154,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane & 31;   // query within the wave (MFMA column)
-  const int half = lane >> 5;  // which half of the K dimension this lane feeds
+  const int half = lane >> 5;  // which half of the MFMA K dimension this lane feeds
 
   const int tile_id = xcd_remap(blockIdx.x, a.grid);
   const int bh = tile_id / a.qblocks;
@@ -111,9 +162,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int N = a.N;
+  const int ntiles = (N + kBlockN - 1) / kBlockN;
 
   const uint16_t* kbase = a.k + b * a.k_sb + h * a.k_sh;
   const uint16_t* vbase = a.v + b * a.v_sb + h * a.v_sh;
+
+  // ---- constant tail of each V row (D = 72): d = 72 holds 1, d = 73..79 hold 0
+  if constexpr (kOnesRow) {
+    for (int r = tid; r < 2 * kBlockN; r += kThreads) {
+      const u32x4 w = {0x3f80u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&lds_v[r / kBlockN][(r % kBlockN) * kVStride + 72]) = w;
+    }
+  }
 
   // ---- this lane's query row as the B operand of S^T = K Q^T
   const int q0 = qb * (32 * NW) + wave * 32;
@@ -138,159 +198,191 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     }
   }
 
-  // ---- cooperative tile loads: global -> registers -> LDS
-  u32x4 kreg[kChunksPerThread], vreg[kChunksPerThread];
-  auto load_tile = [&](int kb) {
+  // ---- cooperative tile staging: global -> registers -> LDS (row-major)
+  u32x4 kreg[kCPT], vreg[kCPT];
+  auto load_rows = [&](const uint16_t* base, int64_t stride, int kb, u32x4* reg) {
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
+    for (int i = 0; i < kCPT; ++i) {
       const int c = tid + i * kThreads;
-      const int row = c / kChunksPerRow, cc = c - row * kChunksPerRow;
+      const int row = c / kCPR, cc = c - row * kCPR;
       const int key = kb + row;
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (c < kChunks && key < N) {
-        kw = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * a.k_st + cc * 8);
-        vw = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(key) * a.v_st + cc * 8);
-      }
-      kreg[i] = kw;
-      vreg[i] = vw;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if ((kChunks % kThreads == 0 || c < kChunks) && key < N)
+        w = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(key) * stride + cc * 8);
+      reg[i] = w;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_rows = [&](uint16_t* tile, int stride, const u32x4* reg) {
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
+    for (int i = 0; i < kCPT; ++i) {
       const int c = tid + i * kThreads;
-      if (c < kChunks) {
-        const int row = c / kChunksPerRow, cc = c - row * kChunksPerRow;
-        *reinterpret_cast<u32x4*>(&lds_k[buf][row * kKStride + cc * 8]) = kreg[i];
-        uint16_t* vt = &lds_v[buf][(cc * 8) * kVStride + row];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vt[(2 * e) * kVStride] = static_cast<uint16_t>(vreg[i][e] & 0xffffu);
-          vt[(2 * e + 1) * kVStride] = static_cast<uint16_t>(vreg[i][e] >> 16);
-        }
+      if (kChunks % kThreads == 0 || c < kChunks) {
+        const int row = c / kCPR, cc = c - row * kCPR;
+        *reinterpret_cast<u32x4*>(&tile[row * stride + cc * 8]) = reg[i];
       }
     }
   };
 
+  // ---- per-lane LDS read offsets (elements)
+  // K operand (A of S^T = K Q^T): row 32*blk + col, columns 16*st + 8*half
+  const int k_off = col * kKStride + 8 * half;
+  const int k_off_tail = col * kKStride + 64 + 4 * half;
+  // V^T operand (A of O^T = V^T P^T) via transpose reads: this lane names
+  // row 16t + 4*half + ((lane>>2)&3) (+8 for the second read) and column
+  // 32*mt + 16*((lane>>4)&1) + 4*(lane&3); the row-sum tile (mt = 2, D = 72)
+  // reads columns 64 + 4*(lane&3) in both 16-lane groups.
+  const int v_row = 4 * half + ((lane >> 2) & 3);
+  const int v_off = v_row * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int v_off_tail = v_row * kVStride + 64 + 4 * (lane & 3);
+
+  const float c = a.c;
+
+  auto qk = [&](const uint16_t* kt, f32x16* s) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(kt + k_off + 32 * blk * kKStride + 16 * st);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[blk], 0, 0, 0);
+      }
+      if constexpr (D == 72) {
+        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt + k_off_tail + 32 * blk * kKStride);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ka, qt, s[blk], 0, 0, 0);
+      }
+    }
+  };
+  // s[blk][r] is the logit of key kb + 32*blk + 8*(r/4) + 4*half + (r%4)
+  auto mask_tail = [&](f32x16* s, int kb) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key >= N) s[blk][r] = -__builtin_inff();
+      }
+  };
+  auto rowmax = [&](const f32x16* s) {
+    float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      m0 = fmaxf(m0, fmaxf(s[0][r], s[0][r + 1]));
+      m1 = fmaxf(m1, fmaxf(s[1][r], s[1][r + 1]));
+    }
+    return max_across_halves(fmaxf(m0, m1));
+  };
+  // probabilities of the 8 keys of PV step t, rounded to bf16
+  float psum = 0.f;
+  auto probs = [&](const f32x16* s, int t, float m) {
+    const int blk = t >> 1, r0 = 8 * (t & 1);
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[blk][r0 + i], c, -m));
+    if constexpr (!kOnesRow) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) psum += p[i];
+    }
+    u32x4 w;
+    w[0] = pack_bf16x2(p[0], p[1]);
+    w[1] = pack_bf16x2(p[2], p[3]);
+    w[2] = pack_bf16x2(p[4], p[5]);
+    w[3] = pack_bf16x2(p[6], p[7]);
+    return __builtin_bit_cast(bf16x8, w);
+  };
   f32x16 acc[kOutTiles];
 #pragma unroll
   for (int t = 0; t < kOutTiles; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;  // per-lane partial row sum (D = 64 only)
-  const float c = a.c;
+  auto pv = [&](const uint16_t* vt, int t, bf16x8 pb) {
+#pragma unroll
+    for (int mt = 0; mt < kOutTiles; ++mt) {
+      const int off = (kOnesRow && mt == 2) ? v_off_tail : v_off + 32 * mt;
+      const uint16_t* p = vt + off + 16 * t * kVStride;
+      const u32x2 lo = lds_read_tr(p);
+      const u32x2 hi = lds_read_tr(p + 8 * kVStride);
+      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb,
+                                                       acc[mt], 0, 0, 0);
+    }
+  };
 
-  const int ntiles = (N + kBlockN - 1) / kBlockN;
-  load_tile(0);
-  store_tile(0);
+  // ---- prologue: K_0, V_0, K_1 in LDS; S_0 and its row max in registers
+  load_rows(kbase, a.k_st, 0, kreg);
+  load_rows(vbase, a.v_st, 0, vreg);
+  store_rows(lds_k[0], kKStride, kreg);
+  store_rows(lds_v[0], kVStride, vreg);
+  if (ntiles > 1) {
+    load_rows(kbase, a.k_st, kBlockN, kreg);
+    store_rows(lds_k[1], kKStride, kreg);
+  }
   __syncthreads();
 
+  f32x16 s_cur[2], s_nxt[2];
+  float mx = 0.f;
+  if (wave_active) {
+    qk(lds_k[0], s_cur);
+    if (kBlockN > N) mask_tail(s_cur, 0);
+    mx = rowmax(s_cur);
+  }
+  // the first loop iteration overwrites K_0's buffer with K_2
+  if (ntiles > 2) __syncthreads();
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;  // per-lane partial row sum (D = 64)
+
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const int kb = j * kBlockN;
-    if (j + 1 < ntiles) load_tile(kb + kBlockN);
+    const bool has_next = j + 1 < ntiles;
+    if (j + 2 < ntiles) load_rows(kbase, a.k_st, (j + 2) * kBlockN, kreg);
+    if (has_next) load_rows(vbase, a.v_st, (j + 1) * kBlockN, vreg);
 
     if (wave_active) {
-      const uint16_t* kt = lds_k[buf];
-      const uint16_t* vt = lds_v[buf];
-      // S^T = K Q^T : two 32-key blocks
-      f32x16 s[2];
+      // lazy running max: move it (and rescale) only when some row's max
+      // grew by more than 2^kLazy
+      const float m_cand = mx * c;
+      const bool grow = m_cand > m_run + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? fast_exp2(m_run - m_cand) : 1.f;
+        m_run = grow ? m_cand : m_run;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+        for (int t = 0; t < kOutTiles; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
-        const uint16_t* krow = kt + (32 * blk + col) * kKStride;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * st + 8 * half);
-          s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[blk], 0, 0, 0);
-        }
-        if constexpr (D == 72) {
-          bf16x4 ka = *reinterpret_cast<const bf16x4*>(krow + 64 + 4 * half);
-          s[blk] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ka, qt, s[blk], 0, 0, 0);
-        }
+          for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+        l_run *= alpha;
       }
-      // s[blk][r] is the logit of key kb + 32*blk + 8*(r/4) + 4*half + (r%4)
-      const bool tail = kb + kBlockN > N;
-      if (tail) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= N) s[blk][r] = -__builtin_inff();
-          }
+      const float m = m_run;
+      const uint16_t* vt = lds_v[j & 1];
+      bf16x8 pb0, pb1, pb2, pb3;
+      // phase 1: Q K^T of tile j+1 alongside the exponentials of tile j
+      if (has_next) qk(lds_k[(j + 1) & 1], s_nxt);
+      pb0 = probs(s_cur, 0, m);
+      pb1 = probs(s_cur, 1, m);
+      pb2 = probs(s_cur, 2, m);
+      // phase 2: first half of P V, last exponentials
+      pv(vt, 0, pb0);
+      pb3 = probs(s_cur, 3, m);
+      pv(vt, 1, pb1);
+      // phase 3: second half of P V alongside the row max of tile j+1
+      pv(vt, 2, pb2);
+      if (has_next) {
+        if ((j + 2) * kBlockN > N) mask_tail(s_nxt, (j + 1) * kBlockN);
+        mx = rowmax(s_nxt);
       }
-      float mx = s[0][0];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-
-      float psum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[blk][r], c, -m_new));
-          if (tail) {
-            const int key = kb + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
-            p = key < N ? p : 0.f;
-          }
-          s[blk][r] = p;
-          if constexpr (!kOnesRow) psum += p;
-        }
-      if constexpr (!kOnesRow) l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int t = 0; t < kOutTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-
-      // O^T += V^T P^T over four 16-key steps.  Step t uses keys
-      // kb + 16t + {4*half + 0..3, 8 + 4*half + 0..3}, which are
-      // s[t/2][8*(t%2) + 0..7] of this lane.
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int blk = t >> 1, r0 = 8 * (t & 1);
-        u32x4 pw;
-        pw[0] = pack_bf16x2(s[blk][r0 + 0], s[blk][r0 + 1]);
-        pw[1] = pack_bf16x2(s[blk][r0 + 2], s[blk][r0 + 3]);
-        pw[2] = pack_bf16x2(s[blk][r0 + 4], s[blk][r0 + 5]);
-        pw[3] = pack_bf16x2(s[blk][r0 + 6], s[blk][r0 + 7]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int mt = 0; mt < kOutTiles; ++mt) {
-          const int d = 32 * mt + col;
-          u32x4 vw;
-          if (d < D) {
-            const uint16_t* vrow = vt + d * kVStride + 16 * t + 4 * half;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-            vw[0] = lo[0];
-            vw[1] = lo[1];
-            vw[2] = hi[0];
-            vw[3] = hi[1];
-          } else {
-            // rows past D: the row d == D is all ones (row sum), others zero
-            const uint32_t one2 = (d == D) ? 0x3f803f80u : 0u;
-            vw[0] = one2;
-            vw[1] = one2;
-            vw[2] = one2;
-            vw[3] = one2;
-          }
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pb,
-                                                           acc[mt], 0, 0, 0);
-        }
+      pv(vt, 3, pb3);
+      if constexpr (!kOnesRow) {
+        l_run += psum;
+        psum = 0.f;
       }
     }
 
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    if (j + 2 < ntiles) store_rows(lds_k[j & 1], kKStride, kreg);
+    if (has_next) store_rows(lds_v[(j + 1) & 1], kVStride, vreg);
     __syncthreads();
+    if (has_next) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) s_cur[blk] = s_nxt[blk];
+    }
   }
 
   if (!wave_active) return;
@@ -298,14 +390,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // ---- epilogue: O = acc / l, bf16, rows < N only
   float l;
   if constexpr (kOnesRow) {
-    // row D sits in output tile D/32 at register 4*((D%32)/8) + (D%4) of the
-    // lanes with half == ((D%8)/4)
-    constexpr int kT = D / 32, kR = 4 * ((D % 32) / 8) + (D % 4), kHalf = (D % 8) / 4;
-    const float mine = acc[kT][kR];
-    const float other = __shfl_xor(mine, 32);
-    l = (half == kHalf) ? mine : other;
+    // row D sits in output tile 2, register 4, of the lanes with half == 0
+    l = lower_half_value(acc[2][4]);
   } else {
-    l = l_run + __shfl_xor(l_run, 32);
+    l = sum_across_halves(l_run);
   }
   const float inv = 1.0f / l;
   if (qi < N) {
@@ -356,7 +444,10 @@ int launch_fwd(const FwdArgs& f, void* stream) {
   ka.o_sb = f.o_sb; ka.o_sh = f.o_sh; ka.o_st = f.o_st;
   ka.H = f.H;
   ka.N = f.N;
-  ka.c = (f.scale < 0.f ? -f.scale : f.scale) * kLog2e;
+  // A zero scale would turn masked (-inf) logits into NaN; any scale below
+  // 1e-30 gives weights exp2(~1e-28) == 1 either way.
+  const float abs_scale = f.scale < 0.f ? -f.scale : f.scale;
+  ka.c = (abs_scale > 1e-30f ? abs_scale : 1e-30f) * kLog2e;
   ka.qsign = f.scale < 0.f ? 0x80008000u : 0u;
   const int nw = pick_waves(f.B, f.H, f.N);
   ka.qblocks = (f.N + 32 * nw - 1) / (32 * nw);
