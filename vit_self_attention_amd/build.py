@@ -22,6 +22,11 @@ FLAGS = [
     "-shared",
     "-fPIC",
     "-Wall",
+    # the kernels never see NaN inputs; max() then needs no NaN quieting
+    "-fno-honor-nans",
+    # MFMA accumulators in ordinary VGPRs: the softmax reads the Q K^T tiles
+    # and rescales the output accumulator without AGPR round trips
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 VALU forms stay off: hipcc must not emit them for this code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

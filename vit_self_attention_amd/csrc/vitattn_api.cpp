@@ -45,6 +45,10 @@ extern "C" int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, v
   const int64_t rows = static_cast<int64_t>(B) * H * N;  // (b, h, token) rows
   if (rows > (int64_t(1) << 40)) return VITATTN_ERR_TOO_LARGE;
   const int64_t pairs = static_cast<int64_t>(B) * H;
+  // a key tile (64 token rows) must span less than 2 GiB: the kernel
+  // addresses its rows with 32-bit byte offsets
+  const int64_t token_stride = layout == VITATTN_LAYOUT_PACKED_BN3HD ? 3 * static_cast<int64_t>(H) * D : D;
+  if (64 * token_stride * 2 >= (int64_t(1) << 31)) return VITATTN_ERR_TOO_LARGE;
   if (pairs * ((static_cast<int64_t>(N) + 31) / 32) > (int64_t(1) << 30))
     return VITATTN_ERR_TOO_LARGE;
 

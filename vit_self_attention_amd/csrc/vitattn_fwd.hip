@@ -28,8 +28,7 @@
 //     are issued while the exponentials of tile j run on the VALU, and the
 //     P V products of tile j overlap the row max of tile j+1;
 //   * online softmax in base 2 with a lazy running max: the accumulator is
-//     rescaled only when a row's max grows by more than 2^8, which keeps
-//     every probability weight <= 256;
+//     rescaled only when a row's max grows by more than 2^64;
 //   * D = 72: the P V product runs three 32-row output tiles (d 0..95); the
 //     spare row d = 72 reads a column of ones stored after each V row, so
 //     the softmax denominator comes out of the same MFMA from the same bf16
@@ -56,7 +55,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kBlockN = 64;           // keys per tile
 constexpr int kKStride = 72;          // K row stride in LDS (elements): 144 B
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;         // rescale only when the max grows by > 2^8
+// The running max is lazy: it moves (and the accumulator is rescaled) only
+// when a row's max grows by more than 2^kLazy.  Weights then stay below
+// 2^64 and row sums below N * 2^64, far inside fp32 range, while bf16
+// rounding of a weight is relative and so independent of the shift.
+constexpr float kLazy = 64.0f;
 
 struct KernelArgs {
   const uint16_t* q;
@@ -137,22 +140,31 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
-  constexpr int kThreads = 64 * NW;
-  constexpr int kCPR = D / 8;                       // 16-byte chunks per row
-  constexpr int kChunks = kBlockN * kCPR;           // chunks per tile
-  constexpr int kCPT = (kChunks + kThreads - 1) / kThreads;
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
   constexpr int kOutTiles = kOnesRow ? 3 : 2;
   constexpr int kVStride = kOnesRow ? 80 : 72;      // V row: D values (+ [1,0,..,0] for D = 72)
-  constexpr int kKTile = kBlockN * kKStride;
+  constexpr int kKTile = kBlockN * kKStride;        // elements
   constexpr int kVTile = kBlockN * kVStride;
+  constexpr int kStageElems = kKTile + kVTile;
+  // LDS ring: tile t lives in stage t % kStages; a tile is fetched three
+  // tiles ahead of the one being reduced.
+  constexpr int kStages = 4;
+  // Direct-to-LDS fetches: each wave instruction moves 64 lanes x 16 B into
+  // 64 consecutive 16-byte LDS slots.  K uses 9 slots per row, V 9 (D = 64)
+  // or 10 (D = 72); slots past the D values of a row are never fetched.
+  constexpr int kKSlotsRow = kKStride / 8, kVSlotsRow = kVStride / 8;
+  constexpr int kKInstr = kBlockN * kKSlotsRow / 64;
+  constexpr int kVInstr = kBlockN * kVSlotsRow / 64;
+  constexpr int kInstr = kKInstr + kVInstr;
+  constexpr int kPerWave = (kInstr + NW - 1) / NW;   // fetch instructions of the busiest wave
+  constexpr int kMinPerWave = kInstr / NW;           // ... and of the least busy one
+  static_assert(kBlockN * kKSlotsRow % 64 == 0 && kBlockN * kVSlotsRow % 64 == 0, "slots");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVTile];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;   // query within the wave (MFMA column)
   const int half = lane >> 5;  // which half of the MFMA K dimension this lane feeds
 
@@ -169,9 +181,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 
   // ---- constant tail of each V row (D = 72): d = 72 holds 1, d = 73..79 hold 0
   if constexpr (kOnesRow) {
-    for (int r = tid; r < 2 * kBlockN; r += kThreads) {
+    for (int r = tid; r < kStages * kBlockN; r += 64 * NW) {
       const u32x4 w = {0x3f80u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&lds_v[r / kBlockN][(r % kBlockN) * kVStride + 72]) = w;
+      *reinterpret_cast<u32x4*>(
+          &lds[(r / kBlockN) * kStageElems + kKTile + (r % kBlockN) * kVStride + 72]) = w;
     }
   }
 
@@ -198,29 +211,61 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     }
   }
 
-  // ---- cooperative tile staging: global -> registers -> LDS (row-major)
-  u32x4 kreg[kCPT], vreg[kCPT];
-  auto load_rows = [&](const uint16_t* base, int64_t stride, int kb, u32x4* reg) {
+  // ---- direct-to-LDS tile fetch.  Fetch instruction i of this wave is
+  // number I = i*NW + wave of the tile: I < kKInstr fills K slots, the rest
+  // V slots.  Slot s of a row-major LDS tile holds row s / slots_per_row,
+  // 16-byte column s % slots_per_row.  In the last tile, rows past N repeat
+  // row N-1 (finite data that the mask or a zero weight removes).
+  const int k_st32 = static_cast<int>(a.k_st), v_st32 = static_cast<int>(a.v_st);
+  uint32_t f_off[kPerWave];  // byte offset of this lane's chunk from the tile's first row
+  int f_rc[kPerWave];        // row | column << 8; column >= D/8 marks a slot never fetched
 #pragma unroll
-    for (int i = 0; i < kCPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / kCPR, cc = c - row * kCPR;
-      const int key = kb + row;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if ((kChunks % kThreads == 0 || c < kChunks) && key < N)
-        w = *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(key) * stride + cc * 8);
-      reg[i] = w;
-    }
-  };
-  auto store_rows = [&](uint16_t* tile, int stride, const u32x4* reg) {
+  for (int i = 0; i < kPerWave; ++i) {
+    const int I = i * NW + wave;
+    const bool is_k = I < kKInstr;
+    const int slot = (is_k ? I : I - kKInstr) * 64 + lane;
+    const int per_row = is_k ? kKSlotsRow : kVSlotsRow;
+    const int row = slot / per_row, cc = slot - (slot / per_row) * per_row;
+    f_rc[i] = row | (cc << 8);
+    f_off[i] = static_cast<uint32_t>((row * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
+  }
+  auto fetch_tile = [&](int t) {
+    uint16_t* stage = lds + (t & (kStages - 1)) * kStageElems;
+    const int kb = t * kBlockN;
+    const char* gk = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st);
+    const char* gv = reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
+    const bool tail = kb + kBlockN > N;
+    const int last = N - 1 - kb;
 #pragma unroll
-    for (int i = 0; i < kCPT; ++i) {
-      const int c = tid + i * kThreads;
-      if (kChunks % kThreads == 0 || c < kChunks) {
-        const int row = c / kCPR, cc = c - row * kCPR;
-        *reinterpret_cast<u32x4*>(&tile[row * stride + cc * 8]) = reg[i];
+    for (int i = 0; i < kPerWave; ++i) {
+      const int I = i * NW + wave;
+      if (I < kInstr) {
+        const bool is_k = I < kKInstr;
+        uint16_t* dst = is_k ? stage + I * 512 : stage + kKTile + (I - kKInstr) * 512;
+        const int cc = f_rc[i] >> 8;
+        if (cc < D / 8) {
+          uint32_t off = f_off[i];
+          if (tail) {
+            const int row = f_rc[i] & 255;
+            const int r = row < last ? row : last;
+            off = static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
+          }
+          const char* src = (is_k ? gk : gv) + off;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                           (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
       }
     }
+  };
+  // Waits until at most `n` fetch instructions of this wave are in flight
+  // (vector-memory counter; the other counters are left alone), then meets
+  // the rest of the workgroup.  The memory clobber keeps LDS reads after it.
+  auto wait_fetch_and_sync = [&](bool one_tile_in_flight) {
+    if (one_tile_in_flight)
+      __builtin_amdgcn_s_waitcnt((kMinPerWave & 15) | ((kMinPerWave >> 4) << 14) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    asm volatile("s_barrier" ::: "memory");
   };
 
   // ---- per-lane LDS read offsets (elements)
@@ -265,30 +310,42 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       }
   };
   auto rowmax = [&](const f32x16* s) {
-    float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
+    // 32 values through a tree of three-input maxima
+    float m[8];
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      m0 = fmaxf(m0, fmaxf(s[0][r], s[0][r + 1]));
-      m1 = fmaxf(m1, fmaxf(s[1][r], s[1][r + 1]));
+    for (int i = 0; i < 8; ++i) {
+      const f32x16& v = s[i >> 2];
+      const int r = 4 * (i & 3);
+      m[i] = fmaxf(fmaxf(v[r], v[r + 1]), fmaxf(v[r + 2], v[r + 3]));
     }
-    return max_across_halves(fmaxf(m0, m1));
+    const float a0 = fmaxf(fmaxf(m[0], m[1]), m[2]);
+    const float a1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
+    const float a2 = fmaxf(m[6], m[7]);
+    return max_across_halves(fmaxf(fmaxf(a0, a1), a2));
   };
-  // probabilities of the 8 keys of PV step t, rounded to bf16
+  // probabilities of the 8 keys of PV step t, rounded to bf16.  For D = 64
+  // the row sum adds up the same bf16 values (dot products with ones, fp32
+  // accumulation), so numerator and denominator use identical weights.
   float psum = 0.f;
   auto probs = [&](const f32x16* s, int t, float m) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const int blk = t >> 1, r0 = 8 * (t & 1);
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[blk][r0 + i], c, -m));
-    if constexpr (!kOnesRow) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) psum += p[i];
-    }
     u32x4 w;
     w[0] = pack_bf16x2(p[0], p[1]);
     w[1] = pack_bf16x2(p[2], p[3]);
     w[2] = pack_bf16x2(p[4], p[5]);
     w[3] = pack_bf16x2(p[6], p[7]);
+    if constexpr (!kOnesRow) {
+      const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wi = w[i];
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), ones, psum, false);
+      }
+    }
     return __builtin_bit_cast(bf16x8, w);
   };
   f32x16 acc[kOutTiles];
@@ -309,33 +366,27 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     }
   };
 
-  // ---- prologue: K_0, V_0, K_1 in LDS; S_0 and its row max in registers
-  load_rows(kbase, a.k_st, 0, kreg);
-  load_rows(vbase, a.v_st, 0, vreg);
-  store_rows(lds_k[0], kKStride, kreg);
-  store_rows(lds_v[0], kVStride, vreg);
-  if (ntiles > 1) {
-    load_rows(kbase, a.k_st, kBlockN, kreg);
-    store_rows(lds_k[1], kKStride, kreg);
-  }
-  __syncthreads();
+  // ---- prologue: fetch tiles 0..2; S_0 and its row max in registers
+  fetch_tile(0);
+  if (ntiles > 1) fetch_tile(1);
+  if (ntiles > 2) fetch_tile(2);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // the V ones column (LDS stores) is written
+  wait_fetch_and_sync(ntiles > 2);      // tiles 0 and 1 have landed
 
   f32x16 s_cur[2], s_nxt[2];
   float mx = 0.f;
   if (wave_active) {
-    qk(lds_k[0], s_cur);
+    qk(lds, s_cur);
     if (kBlockN > N) mask_tail(s_cur, 0);
     mx = rowmax(s_cur);
   }
-  // the first loop iteration overwrites K_0's buffer with K_2
-  if (ntiles > 2) __syncthreads();
   float m_run = -__builtin_inff();
   float l_run = 0.f;  // per-lane partial row sum (D = 64)
 
   for (int j = 0; j < ntiles; ++j) {
     const bool has_next = j + 1 < ntiles;
-    if (j + 2 < ntiles) load_rows(kbase, a.k_st, (j + 2) * kBlockN, kreg);
-    if (has_next) load_rows(vbase, a.v_st, (j + 1) * kBlockN, vreg);
+    // stage (j+3)%4 held tile j-1, whose reads all ended before the last barrier
+    if (j + 3 < ntiles) fetch_tile(j + 3);
 
     if (wave_active) {
       // lazy running max: move it (and rescale) only when some row's max
@@ -352,10 +403,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         l_run *= alpha;
       }
       const float m = m_run;
-      const uint16_t* vt = lds_v[j & 1];
+      const uint16_t* vt = lds + (j & (kStages - 1)) * kStageElems + kKTile;
       bf16x8 pb0, pb1, pb2, pb3;
       // phase 1: Q K^T of tile j+1 alongside the exponentials of tile j
-      if (has_next) qk(lds_k[(j + 1) & 1], s_nxt);
+      if (has_next) qk(lds + ((j + 1) & (kStages - 1)) * kStageElems, s_nxt);
       pb0 = probs(s_cur, 0, m);
       pb1 = probs(s_cur, 1, m);
       pb2 = probs(s_cur, 2, m);
@@ -376,9 +427,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       }
     }
 
-    if (j + 2 < ntiles) store_rows(lds_k[j & 1], kKStride, kreg);
-    if (has_next) store_rows(lds_v[(j + 1) & 1], kVStride, vreg);
-    __syncthreads();
+    // tile j+2 must have landed before the next iteration reads its K
+    if (j + 1 < ntiles) wait_fetch_and_sync(j + 3 < ntiles);
     if (has_next) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) s_cur[blk] = s_nxt[blk];
