@@ -43,7 +43,25 @@ def _parse():
                    help="skip the 384 px SigLIP (B=48, N=729) figures")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline")
+    p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times "
+                        "(reference for HBM byte counters) and exit")
     return p.parse_args()
+
+
+def _copy_calibration(mib):
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counter
+    readings calibrate the counters against true bytes moved."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "bytes_read_per_copy": n * 4,
+                      "bytes_written_per_copy": n * 4}), flush=True)
 
 
 def _device_inputs(wl, device, layers):
@@ -77,7 +95,10 @@ def _roofline(wl, launch_s):
 
 
 def _time_steps(va, wl, ins, outs, steps, warmup, stream):
-    """Warmup, then exactly `steps` timed steps; per-launch events as well."""
+    """Warmup, then exactly `steps` timed steps bracketed by two events on the
+    launch stream.  A second pass of the same steps records an event pair
+    around every launch, giving the kernel's own average duration (kept out
+    of the timed region so that event records do not slow the steps)."""
     import torch
 
     def step(evs=None):
@@ -91,19 +112,23 @@ def _time_steps(va, wl, ins, outs, steps, warmup, stream):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    L = len(ins)
-    launch_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
-                  for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for k in range(steps):
-        step(launch_evs[k])
+    for _ in range(steps):
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+
+    L = len(ins)
+    launch_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+                  for _ in range(steps)]
+    for k in range(steps):
+        step(launch_evs[k])
+    torch.cuda.synchronize()
     launch_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in launch_evs for i in range(L)]
     return total_ms, launch_ms, wall
 
@@ -158,6 +183,9 @@ def _trimmed_median(xs):
 
 def main():
     args = _parse()
+    if args.copy_calib:
+        _copy_calibration(args.copy_calib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
               "forward shards over images with no communication, so the single-GPU "
@@ -213,12 +241,7 @@ def main():
     if not args.no_target and wl.key != "c5":
         t = WORKLOADS["c5"]
         tins, touts, _ = _device_inputs(t, device, 1)
-        samples = []
-        for _ in range(3):
-            _time_steps(va, t, tins, touts, 1, 1, stream)
-        for _ in range(50):
-            tot, lm, _ = _time_steps(va, t, tins, touts, 1, 0, stream)
-            samples.append(lm[0])
+        _, samples, _ = _time_steps(va, t, tins, touts, 50, 5, stream)
         us = _trimmed_median(samples) * 1e3
         tf = t.flops_per_layer / (us * 1e-6) / 1e12
         result["siglip384_target"] = {

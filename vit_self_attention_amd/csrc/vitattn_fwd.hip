@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "vitattn.h"
 #include "vitattn_internal.h"
 
@@ -146,9 +148,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr int kKTile = kBlockN * kKStride;        // elements
   constexpr int kVTile = kBlockN * kVStride;
   constexpr int kStageElems = kKTile + kVTile;
-  // LDS ring: tile t lives in stage t % kStages; a tile is fetched three
-  // tiles ahead of the one being reduced.
-  constexpr int kStages = 4;
+  // LDS ring: tile t lives in stage t % kStages and is fetched kStages-1
+  // tiles ahead of the one being reduced (8-wave workgroups own the whole
+  // LDS of a compute unit and use a deeper ring).
+  constexpr int kStages = NW >= 8 ? 8 : 4;
   // Direct-to-LDS fetches: each wave instruction moves 64 lanes x 16 B into
   // 64 consecutive 16-byte LDS slots.  K uses 9 slots per row, V 9 (D = 64)
   // or 10 (D = 72); slots past the D values of a row are never fetched.
@@ -229,44 +232,52 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     f_rc[i] = row | (cc << 8);
     f_off[i] = static_cast<uint32_t>((row * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
   }
-  auto fetch_tile = [&](int t) {
-    uint16_t* stage = lds + (t & (kStages - 1)) * kStageElems;
+  // issues fetch instruction i of tile t (nothing for waves with fewer)
+  auto fetch_one = [&](int t, int i) __attribute__((always_inline)) {
+    const int I = i * NW + wave;
+    if (I >= kInstr) return;
+    uint16_t* stage = lds + (t % kStages) * kStageElems;
     const int kb = t * kBlockN;
-    const char* gk = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st);
-    const char* gv = reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
-    const bool tail = kb + kBlockN > N;
-    const int last = N - 1 - kb;
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int I = i * NW + wave;
-      if (I < kInstr) {
-        const bool is_k = I < kKInstr;
-        uint16_t* dst = is_k ? stage + I * 512 : stage + kKTile + (I - kKInstr) * 512;
-        const int cc = f_rc[i] >> 8;
-        if (cc < D / 8) {
-          uint32_t off = f_off[i];
-          if (tail) {
-            const int row = f_rc[i] & 255;
-            const int r = row < last ? row : last;
-            off = static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
-          }
-          const char* src = (is_k ? gk : gv) + off;
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                           (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        }
+    const bool is_k = I < kKInstr;
+    const char* g = is_k ? reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st)
+                         : reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
+    uint16_t* dst = is_k ? stage + I * 512 : stage + kKTile + (I - kKInstr) * 512;
+    const int cc = f_rc[i] >> 8;
+    if (cc < D / 8) {
+      uint32_t off = f_off[i];
+      if (kb + kBlockN > N) {
+        const int last = N - 1 - kb;
+        const int row = f_rc[i] & 255;
+        const int r = row < last ? row : last;
+        off = static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
       }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
+  };
+  auto fetch_tile = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) fetch_one(t, i);
   };
   // Waits until at most `n` fetch instructions of this wave are in flight
   // (vector-memory counter; the other counters are left alone), then meets
   // the rest of the workgroup.  The memory clobber keeps LDS reads after it.
-  auto wait_fetch_and_sync = [&](bool one_tile_in_flight) {
-    if (one_tile_in_flight)
-      __builtin_amdgcn_s_waitcnt((kMinPerWave & 15) | ((kMinPerWave >> 4) << 14) | (7 << 4) | (15 << 8));
-    else
-      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  auto wait_fetch_and_sync = [&](int tiles_in_flight) __attribute__((always_inline)) {
+    // vmcnt(n) only (expcnt 7, lgkmcnt 15 mean "no wait" for those counters)
+#define VITATTN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+    switch (tiles_in_flight) {
+      case 0: VITATTN_WAIT_VM(0); break;
+      case 1: VITATTN_WAIT_VM(kMinPerWave); break;
+      case 2: VITATTN_WAIT_VM(2 * kMinPerWave); break;
+      case 3: VITATTN_WAIT_VM(3 * kMinPerWave); break;
+      case 4: VITATTN_WAIT_VM(4 * kMinPerWave); break;
+      default: VITATTN_WAIT_VM(5 * kMinPerWave); break;
+    }
+#undef VITATTN_WAIT_VM
     asm volatile("s_barrier" ::: "memory");
   };
+  // tiles fetched after tile t, at the point where the fetch of tile `issued` is the last one
+  auto after = [&](int t, int issued) { return issued > t ? issued - t : 0; };
 
   // ---- per-lane LDS read offsets (elements)
   // K operand (A of S^T = K Q^T): row 32*blk + col, columns 16*st + 8*half
@@ -282,111 +293,81 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 
   const float c = a.c;
 
-  auto qk = [&](const uint16_t* kt, f32x16* s) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(kt + k_off + 32 * blk * kKStride + 16 * st);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[blk], 0, 0, 0);
-      }
-      if constexpr (D == 72) {
-        const bf16x4 ka = *reinterpret_cast<const bf16x4*>(kt + k_off_tail + 32 * blk * kKStride);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ka, qt, s[blk], 0, 0, 0);
-      }
-    }
+  // ---- building blocks of one key tile
+  // K operand of Q K^T step i (i < 8: columns 16*(i/2) of key block i%2;
+  // D = 72 adds steps 8, 9 over columns 64..71 with the 32x32x8 shape)
+  auto k_read = [&](const uint16_t* kt, int i) {
+    return *reinterpret_cast<const bf16x8*>(kt + k_off + 32 * (i & 1) * kKStride + 16 * (i >> 1));
   };
-  // s[blk][r] is the logit of key kb + 32*blk + 8*(r/4) + 4*half + (r%4)
-  auto mask_tail = [&](f32x16* s, int kb) {
+  auto k_read_tail = [&](const uint16_t* kt, int blk) {
+    return *reinterpret_cast<const bf16x4*>(kt + k_off_tail + 32 * blk * kKStride);
+  };
+  auto qk_plain = [&](const uint16_t* kt, f32x16* s) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key >= N) s[blk][r] = -__builtin_inff();
-      }
-  };
-  auto rowmax = [&](const f32x16* s) {
-    // 32 values through a tree of three-input maxima
-    float m[8];
+      for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x16& v = s[i >> 2];
-      const int r = 4 * (i & 3);
-      m[i] = fmaxf(fmaxf(v[r], v[r + 1]), fmaxf(v[r + 2], v[r + 3]));
+    for (int i = 0; i < 8; ++i)
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(kt, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+    if constexpr (D == 72) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(k_read_tail(kt, blk), qt, s[blk], 0, 0, 0);
     }
-    const float a0 = fmaxf(fmaxf(m[0], m[1]), m[2]);
-    const float a1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
-    const float a2 = fmaxf(m[6], m[7]);
-    return max_across_halves(fmaxf(fmaxf(a0, a1), a2));
   };
-  // probabilities of the 8 keys of PV step t, rounded to bf16.  For D = 64
-  // the row sum adds up the same bf16 values (dot products with ones, fp32
-  // accumulation), so numerator and denominator use identical weights.
-  float psum = 0.f;
-  auto probs = [&](const f32x16* s, int t, float m) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const int blk = t >> 1, r0 = 8 * (t & 1);
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(s[blk][r0 + i], c, -m));
-    u32x4 w;
-    w[0] = pack_bf16x2(p[0], p[1]);
-    w[1] = pack_bf16x2(p[2], p[3]);
-    w[2] = pack_bf16x2(p[4], p[5]);
-    w[3] = pack_bf16x2(p[6], p[7]);
-    if constexpr (!kOnesRow) {
-      const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wi = w[i];
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), ones, psum, false);
-      }
-    }
+  // V^T operand of P V step idx = t*kOutTiles + mt (keys 16t.., output rows 32mt..)
+  auto v_read = [&](const uint16_t* vt, int idx) {
+    const int t = idx / kOutTiles, mt = idx % kOutTiles;
+    const int off = (kOnesRow && mt == 2) ? v_off_tail : v_off + 32 * mt;
+    const uint16_t* p = vt + off + 16 * t * kVStride;
+    const u32x2 lo = lds_read_tr(p);
+    const u32x2 hi = lds_read_tr(p + 8 * kVStride);
+    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
     return __builtin_bit_cast(bf16x8, w);
   };
+  // s[blk][r] is the logit of key kb + 32*blk + 8*(r/4) + 4*half + (r%4);
+  // element e = 16*blk + r, and P V step t uses elements 8t .. 8t+7.
+  auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * half + (e & 3); };
+  // partial row max over elements 4g .. 4g+3
+  auto max4 = [&](const f32x16* s, int g) {
+    const f32x16& v = s[g >> 2];
+    const int r = 4 * (g & 3);
+    return fmaxf(fmaxf(v[r], v[r + 1]), fmaxf(v[r + 2], v[r + 3]));
+  };
+  auto rowmax = [&](const f32x16* s) {
+    float m[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) m[g] = max4(s, g);
+    return max_across_halves(
+        fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7]))));
+  };
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  float psum = 0.f;  // D = 64: row sum of the bf16 weights (dot products with ones)
   f32x16 acc[kOutTiles];
 #pragma unroll
   for (int t = 0; t < kOutTiles; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  auto pv = [&](const uint16_t* vt, int t, bf16x8 pb) {
-#pragma unroll
-    for (int mt = 0; mt < kOutTiles; ++mt) {
-      const int off = (kOnesRow && mt == 2) ? v_off_tail : v_off + 32 * mt;
-      const uint16_t* p = vt + off + 16 * t * kVStride;
-      const u32x2 lo = lds_read_tr(p);
-      const u32x2 hi = lds_read_tr(p + 8 * kVStride);
-      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb,
-                                                       acc[mt], 0, 0, 0);
-    }
-  };
-
-  // ---- prologue: fetch tiles 0..2; S_0 and its row max in registers
-  fetch_tile(0);
-  if (ntiles > 1) fetch_tile(1);
-  if (ntiles > 2) fetch_tile(2);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // the V ones column (LDS stores) is written
-  wait_fetch_and_sync(ntiles > 2);      // tiles 0 and 1 have landed
-
-  f32x16 s_cur[2], s_nxt[2];
   float mx = 0.f;
-  if (wave_active) {
-    qk(lds, s_cur);
-    if (kBlockN > N) mask_tail(s_cur, 0);
-    mx = rowmax(s_cur);
-  }
   float m_run = -__builtin_inff();
   float l_run = 0.f;  // per-lane partial row sum (D = 64)
 
-  for (int j = 0; j < ntiles; ++j) {
-    const bool has_next = j + 1 < ntiles;
-    // stage (j+3)%4 held tile j-1, whose reads all ended before the last barrier
-    if (j + 3 < ntiles) fetch_tile(j + 3);
+  // ---- one key tile j.  `cur` holds the logits of tile j; when kNext,
+  // the logits of tile j+1 go to `nxt` and their row max to mx.  kRagged
+  // (last tile, N not a multiple of 64) zeroes the weights of keys >= N.
+  // The body is issued in chunks fenced by sched_barrier: each chunk pairs
+  // one MFMA with the LDS reads of the MFMA two steps later and a share of
+  // the VALU work (exponentials, bf16 packing, maxima), so the VALU runs
+  // while the matrix core works.
+  auto step = [&](int j, f32x16* cur, f32x16* nxt, auto kNextC, auto kRaggedC) __attribute__((always_inline)) {
+    constexpr bool kNext = decltype(kNextC)::value;
+    constexpr bool kRagged = decltype(kRaggedC)::value;
+    // stage (j-1) % kStages held tile j-1, whose reads all ended before the
+    // last barrier; it is refilled with tile j + kStages - 1
+    const int tf = j + kStages - 1;
+    if (tf < ntiles) fetch_tile(tf);
 
     if (wave_active) {
       // lazy running max: move it (and rescale) only when some row's max
@@ -402,37 +383,131 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
           for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
         l_run *= alpha;
       }
-      const float m = m_run;
-      const uint16_t* vt = lds + (j & (kStages - 1)) * kStageElems + kKTile;
-      bf16x8 pb0, pb1, pb2, pb3;
-      // phase 1: Q K^T of tile j+1 alongside the exponentials of tile j
-      if (has_next) qk(lds + ((j + 1) & (kStages - 1)) * kStageElems, s_nxt);
-      pb0 = probs(s_cur, 0, m);
-      pb1 = probs(s_cur, 1, m);
-      pb2 = probs(s_cur, 2, m);
-      // phase 2: first half of P V, last exponentials
-      pv(vt, 0, pb0);
-      pb3 = probs(s_cur, 3, m);
-      pv(vt, 1, pb1);
-      // phase 3: second half of P V alongside the row max of tile j+1
-      pv(vt, 2, pb2);
-      if (has_next) {
-        if ((j + 2) * kBlockN > N) mask_tail(s_nxt, (j + 1) * kBlockN);
-        mx = rowmax(s_nxt);
+      const float neg_m = -m_run;
+      const int kb = j * kBlockN;
+      const uint16_t* kt = lds + ((j + 1) % kStages) * kStageElems;
+      const uint16_t* vt = lds + (j % kStages) * kStageElems + kKTile;
+
+      float p[32];
+      uint32_t w[16];
+      auto do_exp = [&](int e) {
+        p[e] = fast_exp2(__builtin_fmaf(cur[e >> 4][e & 15], c, neg_m));
+        if constexpr (kRagged) p[e] = kb + key_of(e) < N ? p[e] : 0.f;
+        if (e & 1) {
+          const int k = e >> 1;
+          w[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+          if constexpr (!kOnesRow)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]), ones2, psum,
+                                                   false);
+        }
+      };
+      auto pb = [&](int t) {
+        const u32x4 v = {w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
+        return __builtin_bit_cast(bf16x8, v);
+      };
+
+      // phase 1: Q K^T of tile j+1 with the weights of keys 0..47 of tile j
+      constexpr int kQk = D == 72 ? 10 : 8;
+      if constexpr (kNext) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) nxt[blk][r] = 0.f;
+        bf16x8 ko[8];
+        bf16x4 ko4[2];
+        auto fetch_k = [&](int i) {
+          if (i < 8) ko[i] = k_read(kt, i);
+          else ko4[i - 8] = k_read_tail(kt, i - 8);
+        };
+        fetch_k(0);
+        fetch_k(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kQk; ++i) {
+          if (i + 2 < kQk) fetch_k(i + 2);
+          if (i < 8)
+            nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[i], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+          else
+            nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ko4[i - 8], qt, nxt[i & 1], 0, 0, 0);
+#pragma unroll
+          for (int e = 24 * i / kQk; e < 24 * (i + 1) / kQk; ++e) do_exp(e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 24; ++e) do_exp(e);
       }
-      pv(vt, 3, pb3);
+
+      // phases 2 and 3: P V of tile j; the remaining weights ride along the
+      // first half, the row max of tile j+1 the second half
+      constexpr int kPv = 4 * kOutTiles, kHalfPv = 2 * kOutTiles;
+      bf16x8 vo[kPv];
+      vo[0] = v_read(vt, 0);
+      vo[1] = v_read(vt, 1);
+      float gm[8];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kPv; ++i) {
+        if (i + 2 < kPv) vo[i + 2] = v_read(vt, i + 2);
+        const int t = i / kOutTiles, mt = i % kOutTiles;
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[i], pb(t), acc[mt], 0, 0, 0);
+        if (i < kHalfPv) {
+#pragma unroll
+          for (int e = 24 + 8 * i / kHalfPv; e < 24 + 8 * (i + 1) / kHalfPv; ++e) do_exp(e);
+        } else if constexpr (kNext) {
+          const int ii = i - kHalfPv;
+#pragma unroll
+          for (int g = 8 * ii / kHalfPv; g < 8 * (ii + 1) / kHalfPv; ++g) gm[g] = max4(nxt, g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kNext) {
+        mx = max_across_halves(fmaxf(fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3])),
+                                     fmaxf(fmaxf(gm[4], gm[5]), fmaxf(gm[6], gm[7]))));
+      }
       if constexpr (!kOnesRow) {
         l_run += psum;
         psum = 0.f;
       }
     }
 
-    // tile j+2 must have landed before the next iteration reads its K
-    if (j + 1 < ntiles) wait_fetch_and_sync(j + 3 < ntiles);
-    if (has_next) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) s_cur[blk] = s_nxt[blk];
+    // tile j+2 must have landed before the next step reads its K
+    if constexpr (kNext) {
+      const int last_issued = (j + kStages - 1 < ntiles ? j + kStages - 1 : ntiles - 1);
+      wait_fetch_and_sync(after(j + 2, last_issued));
     }
+  };
+
+  // ---- prologue: fetch tiles 0..2; S_0 and its row max in registers.
+  // Keys past N in the last tile hold copies of key N-1 (see fetch_tile),
+  // which leave every row max unchanged; only their weights are zeroed.
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) fetch_tile(t);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // the V ones column (LDS stores) is written
+  // tiles 0 and 1 have landed
+  wait_fetch_and_sync(after(1, (kStages - 2 < ntiles - 1 ? kStages - 2 : ntiles - 1)));
+
+  f32x16 sa[2], sb[2];
+  if (wave_active) {
+    qk_plain(lds, sa);
+    mx = rowmax(sa);
+  }
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+  const bool ragged = N % kBlockN != 0;
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    step(j, sa, sb, True{}, False{});
+    step(j + 1, sb, sa, True{}, False{});
+  }
+  if (j + 1 < ntiles) {
+    step(j, sa, sb, True{}, False{});
+    if (ragged) step(j + 1, sb, sa, False{}, True{});
+    else step(j + 1, sb, sa, False{}, False{});
+  } else {
+    if (ragged) step(j, sa, sb, False{}, True{});
+    else step(j, sa, sb, False{}, False{});
   }
 
   if (!wave_active) return;
@@ -472,7 +547,7 @@ int launch(const KernelArgs& ka, hipStream_t stream) {
 }  // namespace
 
 int pick_waves(int B, int H, int N) {
-  // Largest workgroup (more K/V reuse per LDS tile) that still gives at
+  // The largest workgroup (more K/V reuse per LDS tile) that still gives at
   // least two workgroups per compute unit on the 256-CU part.
   const int64_t pairs = static_cast<int64_t>(B) * H;
   for (int nw = 4; nw > 1; nw >>= 1) {
