@@ -9,7 +9,7 @@ for the default workload, SigLIP-So400m/14 at 224 px with two views
 
 Prints ONE JSON line.  `value` is TFLOP/s over the timed steps (algorithmic
 flops 4*B*H*N^2*D per layer call).  Also reported: us per layer call, the
-roofline of the kernel (per-launch HIP-event timing on the launch stream),
+roofline of the kernel (HIP events on the launch stream),
 the fp64 CPU oracle timed on this host as a baseline, parity of the timed
 outputs with that oracle, and the same figures for the 384 px SigLIP
 workload (B=48, N=729), where the kernel is compute-bound.
@@ -83,31 +83,49 @@ def _device_inputs(wl, device, layers):
     return ins, outs, host
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vitattn_fwd_hbm_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "vit_self_attention_amd", "csrc", "vitattn_fwd.hip")
+
+
+def _measured_traffic(wl):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    runs (calibrated on a plain copy), or None when the kernel source has
+    changed since those counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha or wl.key not in rec.get("workloads", {}):
+        return None
+    return rec["workloads"][wl.key]["bytes_per_launch"]
+
+
 def _roofline(wl, launch_s):
+    """Roofline of the attention kernel: the roof its arithmetic intensity
+    (flops per algorithmic byte) meets first on MI355X."""
     ai = wl.flops_per_layer / wl.bytes_per_layer
+    traffic = _measured_traffic(wl)
     if ai >= RIDGE:
         ach = wl.flops_per_layer / launch_s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic}
     ach = wl.bytes_per_layer / launch_s / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": ach / PEAK_HBM_GBPS, "traffic": None}
+            "frac": ach / PEAK_HBM_GBPS, "traffic": traffic}
 
 
 def _time_steps(va, wl, ins, outs, steps, warmup, stream):
     """Warmup, then exactly `steps` timed steps bracketed by two events on the
-    launch stream.  A second pass of the same steps records an event pair
-    around every launch, giving the kernel's own average duration (kept out
-    of the timed region so that event records do not slow the steps)."""
+    stream the kernels are launched on.  Returns (total ms, wall seconds)."""
     import torch
 
-    def step(evs=None):
-        for i, (ts, o) in enumerate(zip(ins, outs)):
-            if evs is not None:
-                evs[2 * i].record(stream)
+    def step():
+        for ts, o in zip(ins, outs):
             va.fwd(ts[0], ts[1], ts[2], out=o, scale=wl.scale, stream=stream)
-            if evs is not None:
-                evs[2 * i + 1].record(stream)
 
     for _ in range(warmup):
         step()
@@ -120,17 +138,7 @@ def _time_steps(va, wl, ins, outs, steps, warmup, stream):
         step()
     t_end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-
-    L = len(ins)
-    launch_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
-                  for _ in range(steps)]
-    for k in range(steps):
-        step(launch_evs[k])
-    torch.cuda.synchronize()
-    launch_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for evs in launch_evs for i in range(L)]
-    return total_ms, launch_ms, wall
+    return t_start.elapsed_time(t_end), time.perf_counter() - wall0
 
 
 def _cpu_baseline(wl, host, budget_s):
@@ -174,13 +182,6 @@ def _parity(wl, outs_dev, refs):
             "layers": len(refs)}
 
 
-def _trimmed_median(xs):
-    xs = sorted(xs)
-    k = int(len(xs) * 0.05)
-    xs = xs[k:len(xs) - k] if len(xs) > 2 * k else xs
-    return xs[len(xs) // 2]
-
-
 def main():
     args = _parse()
     if args.copy_calib:
@@ -201,10 +202,12 @@ def main():
     wl = WORKLOADS[args.workload]
 
     ins, outs, host = _device_inputs(wl, device, wl.layers)
-    total_ms, launch_ms, wall = _time_steps(va, wl, ins, outs, args.steps, args.warmup, stream)
+    total_ms, wall = _time_steps(va, wl, ins, outs, args.steps, args.warmup, stream)
     ms_per_step = total_ms / args.steps
     value = wl.flops_per_layer * wl.layers / (ms_per_step * 1e-3) / 1e12
-    mean_launch_s = sum(launch_ms) / len(launch_ms) * 1e-3
+    # average duration of one launch over the timed region (back-to-back
+    # launches on one stream, so this includes the dispatch gaps)
+    mean_launch_s = ms_per_step * 1e-3 / wl.layers
     roof = _roofline(wl, mean_launch_s)
 
     result = {
@@ -224,7 +227,6 @@ def main():
                    "layout": "packed [B,N,3,H,D]" if wl.layout == 1 else "separate [B,H,N,D]",
                    "layers_per_step": wl.layers, "scale": wl.scale},
         "us_per_layer": ms_per_step * 1e3 / wl.layers,
-        "us_per_launch_kernel": mean_launch_s * 1e6,
         "mfma_frac": value / PEAK_BF16_TFLOPS,
         "hbm_gbps": wl.bytes_per_layer * wl.layers / (ms_per_step * 1e-3) / 1e9,
         "roofline": roof,
@@ -241,15 +243,15 @@ def main():
     if not args.no_target and wl.key != "c5":
         t = WORKLOADS["c5"]
         tins, touts, _ = _device_inputs(t, device, 1)
-        _, samples, _ = _time_steps(va, t, tins, touts, 50, 5, stream)
-        us = _trimmed_median(samples) * 1e3
+        t_ms, _ = _time_steps(va, t, tins, touts, 50, 5, stream)
+        us = t_ms * 1e3 / 50
         tf = t.flops_per_layer / (us * 1e-6) / 1e12
         result["siglip384_target"] = {
             "workload": t.name, "us_per_layer": us, "tflops": tf,
             "mfma_frac": tf / PEAK_BF16_TFLOPS, "target_frac": 0.40,
             "hbm_gbps": t.bytes_per_layer / (us * 1e-6) / 1e9,
             "roofline": _roofline(t, us * 1e-6),
-            "timing": "per-launch HIP events, median of 50 after 5% trim"}
+            "timing": "50 back-to-back launches between two HIP events, after 5 warmup"}
         del tins, touts
 
     print(json.dumps(result), flush=True)
