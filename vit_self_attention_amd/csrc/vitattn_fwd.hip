@@ -50,6 +50,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -140,7 +141,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return x * q + (x < r ? x : r) + i;
 }
 
-template <int D, int NW>
+// kSplit (short sequences, at most kStages key tiles, NW = 4): the waves of
+// a workgroup share one block of 32 queries, wave w reduces key tile w, and
+// the partial results are merged through LDS at the end.  This gives four
+// times the waves for grids too small to fill the chip.
+template <int D, int NW, bool kSplit>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
   constexpr int kOutTiles = kOnesRow ? 3 : 2;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   }
 
   // ---- this lane's query row as the B operand of S^T = K Q^T
-  const int q0 = qb * (32 * NW) + wave * 32;
+  const int q0 = kSplit ? qb * 32 : qb * (32 * NW) + wave * 32;
   const int qi = q0 + col;
   const bool wave_active = q0 < N;
   bf16x8 qf[4];
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     // stage (j-1) % kStages held tile j-1, whose reads all ended before the
     // last barrier; it is refilled with tile j + kStages - 1
     const int tf = j + kStages - 1;
-    if (tf < ntiles) fetch_tile(tf);
+    if (!kSplit && tf < ntiles) fetch_tile(tf);
 
     if (wave_active) {
       // lazy running max: move it (and rescale) only when some row's max
@@ -478,6 +483,85 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     }
   };
 
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
+  const bool ragged = N % kBlockN != 0;
+  f32x16 sa[2], sb[2];
+
+  if constexpr (kSplit) {
+    // ---- all tiles (at most kStages) in LDS at once; wave w reduces tile w
+#pragma unroll
+    for (int t = 0; t < kStages; ++t)
+      if (t < ntiles) fetch_tile(t);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the V ones column (LDS stores) is written
+    wait_fetch_and_sync(0);
+    const int my = wave;
+    if (wave_active && my < ntiles) {
+      qk_plain(lds + my * kStageElems, sa);
+      mx = rowmax(sa);
+      if (ragged && my == ntiles - 1) step(my, sa, sb, False{}, True{});
+      else step(my, sa, sb, False{}, False{});
+    }
+    // ---- merge the partial results of the waves (each: running max m,
+    // accumulator, and for D = 64 the partial row sum) through LDS, laid out
+    // [wave][group of 4 registers][lane][4] so every access is 1 KB contiguous
+    if (!wave_active) return;  // the whole workgroup shares this predicate
+    constexpr int kGroups = kOutTiles * 4 + 1;         // acc groups + (m, l)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage reads done
+    float* mb = reinterpret_cast<float*>(lds);
+    auto slot = [&](int w, int g) { return mb + ((w * kGroups + g) * 64 + lane) * 4; };
+#pragma unroll
+    for (int mt = 0; mt < kOutTiles; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc[mt][4 * g], acc[mt][4 * g + 1], acc[mt][4 * g + 2], acc[mt][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(slot(wave, mt * 4 + g)) = v;
+      }
+    {
+      const f32x4 v = {m_run, l_run, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(slot(wave, kOutTiles * 4)) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // wave w finalizes register group w of every output tile
+    float mw[4], lw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x4 ml = *reinterpret_cast<const f32x4*>(slot(w, kOutTiles * 4));
+      mw[w] = ml[0];
+      if constexpr (kOnesRow) {
+        // the row sum is output row D: tile 2, register 4, lanes with half 0
+        lw[w] = mb[((w * kGroups + 9) * 64 + col) * 4];
+      } else {
+        lw[w] = ml[1] + mb[((w * kGroups + kOutTiles * 4) * 64 + (lane ^ 32)) * 4 + 1];
+      }
+    }
+    const float mstar = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    float sc[4], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sc[w] = fast_exp2(mw[w] - mstar);  // 0 for waves without a tile (m = -inf)
+      l += sc[w] * lw[w];
+    }
+    const float inv = 1.0f / l;
+    if (qi < N) {
+      uint16_t* orow = a.o + b * a.o_sb + h * a.o_sh + static_cast<int64_t>(qi) * a.o_st;
+#pragma unroll
+      for (int mt = 0; mt < kOutTiles; ++mt) {
+        const int d0 = 32 * mt + 8 * wave + 4 * half;
+        if (d0 < D) {
+          f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) o += sc[w] * *reinterpret_cast<const f32x4*>(slot(w, mt * 4 + wave));
+          u32x2 st;
+          st[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
+          st[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d0) = st;
+        }
+      }
+    }
+    return;
+  }
+
   // ---- prologue: fetch tiles 0..2; S_0 and its row max in registers.
   // Keys past N in the last tile hold copies of key N-1 (see fetch_tile),
   // which leave every row max unchanged; only their weights are zeroed.
@@ -488,14 +572,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // tiles 0 and 1 have landed
   wait_fetch_and_sync(after(1, (kStages - 2 < ntiles - 1 ? kStages - 2 : ntiles - 1)));
 
-  f32x16 sa[2], sb[2];
   if (wave_active) {
     qk_plain(lds, sa);
     mx = rowmax(sa);
   }
-  using True = std::integral_constant<bool, true>;
-  using False = std::integral_constant<bool, false>;
-  const bool ragged = N % kBlockN != 0;
   int j = 0;
   for (; j + 2 < ntiles; j += 2) {
     step(j, sa, sb, True{}, False{});
@@ -538,18 +618,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool kSplit>
 int launch(const KernelArgs& ka, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NW>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka);
   return hipGetLastError() == hipSuccess ? VITATTN_OK : VITATTN_ERR_LAUNCH;
 }
 
 }  // namespace
 
 int pick_waves(int B, int H, int N) {
-  // The largest workgroup (more K/V reuse per LDS tile) that still gives at
-  // least two workgroups per compute unit on the 256-CU part.
+  // Short sequences (2..4 key tiles) on grids too small to fill the chip:
+  // four waves split the keys of one 32-query block (returned as -4).
   const int64_t pairs = static_cast<int64_t>(B) * H;
+  const int ntiles = (N + 63) / 64;
+  if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 31) / 32) < 2048) return -4;
+  // Otherwise the largest workgroup (more K/V reuse per LDS tile) that still
+  // gives at least two workgroups per compute unit on the 256-CU part.
   for (int nw = 4; nw > 1; nw >>= 1) {
     const int64_t qblocks = (N + 32 * nw - 1) / (32 * nw);
     if (pairs * qblocks >= 512) return nw;
@@ -575,17 +659,20 @@ int launch_fwd(const FwdArgs& f, void* stream) {
   ka.c = (abs_scale > 1e-30f ? abs_scale : 1e-30f) * kLog2e;
   ka.qsign = f.scale < 0.f ? 0x80008000u : 0u;
   const int nw = pick_waves(f.B, f.H, f.N);
-  ka.qblocks = (f.N + 32 * nw - 1) / (32 * nw);
+  const int qpb = nw < 0 ? 32 : 32 * nw;  // queries per workgroup
+  ka.qblocks = (f.N + qpb - 1) / qpb;
   ka.grid = f.B * f.H * ka.qblocks;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (f.D == 64) {
-    if (nw == 4) return launch<64, 4>(ka, s);
-    if (nw == 2) return launch<64, 2>(ka, s);
-    return launch<64, 1>(ka, s);
+    if (nw == -4) return launch<64, 4, true>(ka, s);
+    if (nw == 4) return launch<64, 4, false>(ka, s);
+    if (nw == 2) return launch<64, 2, false>(ka, s);
+    return launch<64, 1, false>(ka, s);
   }
-  if (nw == 4) return launch<72, 4>(ka, s);
-  if (nw == 2) return launch<72, 2>(ka, s);
-  return launch<72, 1>(ka, s);
+  if (nw == -4) return launch<72, 4, true>(ka, s);
+  if (nw == 4) return launch<72, 4, false>(ka, s);
+  if (nw == 2) return launch<72, 2, false>(ka, s);
+  return launch<72, 1, false>(ka, s);
 }
 
 }  // namespace vitattn
