@@ -1,0 +1,78 @@
+"""Properties of the compiled gfx950 code that the kernel's correctness or
+speed relies on, checked on the device assembly hipcc writes for it (CPU
+only: the kernel source is compiled with the library's own flags, nothing
+runs on a GPU).
+
+* The direct-to-LDS fetches are written as inline asm that sets M0 itself.
+  That is only safe while nothing else in the kernel uses M0: every M0
+  write must be one of those fetch sequences, with the wait state the
+  hardware needs between the write and the fetch.
+* No kernel may spill to scratch memory, and the four-wave kernels must
+  fit two waves per SIMD (at most 256 registers, VGPRs and AGPRs together).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "vit_self_attention_amd", "csrc")
+
+pytestmark = pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc") and shutil.which("hipcc") is None,
+                                reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    from vit_self_attention_amd import build as b
+    out = tmp_path_factory.mktemp("codegen") / "fwd.s"
+    flags = [f for f in b.FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [b.HIPCC, *flags, "-S", "--cuda-device-only", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-o", str(out), os.path.join(CSRC, "vitattn_fwd.hip")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-4000:]
+    return out.read_text()
+
+
+def _kernels(text):
+    """{kernel symbol: (body instruction lines, metadata tail)}"""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*fwd_kernel\S*):[ \t]*(?:;.*)?$", text, re.M):
+        end = text.index(".Lfunc_end", m.end())
+        body = [ln.strip() for ln in text[m.end():end].splitlines()]
+        body = [ln.split(";")[0].strip() for ln in body if ln and not ln.startswith((";", "."))]
+        out[m.group(1)] = (body, text[end:end + 4000])
+    return out
+
+
+def test_every_kernel_instantiation_found(asm):
+    names = list(_kernels(asm))
+    # D in {64, 72} x (NW in {1, 2, 4} without split, NW = 4 with split)
+    assert len(names) == 8, names
+
+
+def test_m0_is_only_written_by_the_fetch_sequence(asm):
+    for name, (body, _) in _kernels(asm).items():
+        for i, ln in enumerate(body):
+            if "m0" not in ln:
+                continue
+            # the only instruction that names m0 is the asm's own write ...
+            assert re.match(r"s_mov_b32 m0, s\d+$", ln), (name, ln)
+            # ... followed by the wait state and the fetch that reads it
+            assert body[i + 1] == "s_nop 0", (name, body[i:i + 3])
+            assert body[i + 2].startswith("global_load_lds_dwordx4"), (name, body[i:i + 3])
+        fetches = [ln for ln in body if ln.startswith("global_load_lds")]
+        writes = [ln for ln in body if ln.startswith("s_mov_b32 m0")]
+        assert len(fetches) == len(writes) > 0, name
+
+
+def test_no_scratch_and_two_waves_per_simd(asm):
+    for name, (_, meta) in _kernels(asm).items():
+        scratch = int(re.search(r"ScratchSize: (\d+)", meta).group(1))
+        total = int(re.search(r"TotalNumVgprs: (\d+)", meta).group(1))
+        assert scratch == 0, (name, scratch)
+        nw = int(re.search(r"fwd_kernelILi\d+ELi(\d+)E", name).group(1))
+        if nw == 4:
+            assert total <= 256, (name, total)

@@ -11,9 +11,9 @@
 // Work decomposition
 //   * one workgroup per (image, head, block of 32*NW queries); NW waves of
 //     64 lanes, each wave owning 32 queries;
-//   * keys in tiles of 64, loaded cooperatively with 128-bit global loads
-//     and stored row-major in LDS (K two tiles ahead, V one tile ahead of
-//     the tile being reduced, each double-buffered, one barrier per tile);
+//   * keys in tiles of 64, fetched cooperatively with 128-bit direct-to-LDS
+//     loads into a ring of LDS stages (row-major K and V), three tiles ahead
+//     of the tile being reduced, one barrier per tile;
 //   * both products on bf16 MFMA with fp32 accumulation, in transposed form:
 //       S^T = K Q^T       (v_mfma_f32_32x32x16_bf16; D = 72 adds a 32x32x8)
 //       O^T += V^T P^T    (v_mfma_f32_32x32x16_bf16)
@@ -33,8 +33,9 @@
 //     spare row d = 72 reads a column of ones stored after each V row, so
 //     the softmax denominator comes out of the same MFMA from the same bf16
 //     weights that multiply V;
-//   * tails: keys >= N are zero-filled in LDS and masked to -inf in the
-//     last tile only; queries >= N run on zero rows and are never stored.
+//   * tails: keys >= N of the last tile are fetched as copies of key N-1
+//     (so row maxima are unchanged) and get zero weights; queries >= N run
+//     on zero rows and are never stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -131,6 +132,26 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// One direct-to-LDS fetch: every active lane copies 16 bytes from
+// g + off (its own offset) into slot `lane` of the 64 x 16-byte LDS block at
+// byte address lds_addr (wave-uniform, passed in M0).  Written as inline asm so that
+// the compiler does not track it as an LDS store: its own tracking cannot
+// tell the ring stage being filled from the stages being read and would put
+// a full vector-memory wait before every LDS transpose read.  The kernel
+// orders these fetches itself (vmcnt waits and a barrier before a stage is
+// read; a stage is refilled only after the barrier that ends its reads),
+// and the memory clobber keeps LDS accesses from moving across it.  Nothing
+// else in the kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved: the clobber is intended
+__device__ __forceinline__ void dma16(const char* g, uint32_t off, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  // one wait state between the M0 write and the instruction that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(g)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
 // over the 8 XCDs (id mod 8); this bijection gives each XCD a contiguous
 // range of logical tiles, so the query blocks of one (image, head) -- which
@@ -149,7 +170,9 @@ template <int D, int NW, bool kSplit>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
   constexpr int kOutTiles = kOnesRow ? 3 : 2;
-  constexpr int kVStride = kOnesRow ? 80 : 72;      // V row: D values (+ [1,0,..,0] for D = 72)
+  // V row: D values (+ [1,0,..,0] for D = 72) in a 160-byte row; with the key
+  // order below this stride makes the transpose reads free of bank conflicts
+  constexpr int kVStride = 80;
   constexpr int kKTile = kBlockN * kKStride;        // elements
   constexpr int kVTile = kBlockN * kVStride;
   constexpr int kStageElems = kKTile + kVTile;
@@ -169,6 +192,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   static_assert(kBlockN * kKSlotsRow % 64 == 0 && kBlockN * kVSlotsRow % 64 == 0, "slots");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems];
+  // byte address of lds in the LDS aperture (what M0 takes)
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)lds));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,12 +267,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   auto fetch_one = [&](int t, int i) __attribute__((always_inline)) {
     const int I = i * NW + wave;
     if (I >= kInstr) return;
-    uint16_t* stage = lds + (t % kStages) * kStageElems;
     const int kb = t * kBlockN;
     const bool is_k = I < kKInstr;
     const char* g = is_k ? reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st)
                          : reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
-    uint16_t* dst = is_k ? stage + I * 512 : stage + kKTile + (I - kKInstr) * 512;
+    const int dst = (t % kStages) * kStageElems + (is_k ? I * 512 : kKTile + (I - kKInstr) * 512);
     const int cc = f_rc[i] >> 8;
     if (cc < D / 8) {
       uint32_t off = f_off[i];
@@ -256,8 +281,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         const int r = row < last ? row : last;
         off = static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + off),
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      dma16(g, off, lds_base + 2 * dst);
     }
   };
   auto fetch_tile = [&](int t) __attribute__((always_inline)) {
@@ -284,15 +308,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // tiles fetched after tile t, at the point where the fetch of tile `issued` is the last one
   auto after = [&](int t, int issued) { return issued > t ? issued - t : 0; };
 
+  // ---- key order.  Row i of each 32-key block of S^T holds key
+  // krow(i) = 16*(i/16) + perm16(i%16), perm16(8m + 4h + j) = 8m + 2j + h:
+  // a transpose read then touches keys {0,2,4,6} (+8m) in one half of the
+  // wave and {1,3,5,7} in the other, whose 64-byte V row segments land in
+  // disjoint LDS banks at a 160-byte row stride.  The order is invisible
+  // outside: K rows and V rows are read in the same order.
+  auto krow = [](int i) { return 16 * (i >> 4) + 8 * ((i >> 3) & 1) + 2 * (i & 3) + ((i >> 2) & 1); };
   // ---- per-lane LDS read offsets (elements)
-  // K operand (A of S^T = K Q^T): row 32*blk + col, columns 16*st + 8*half
-  const int k_off = col * kKStride + 8 * half;
-  const int k_off_tail = col * kKStride + 64 + 4 * half;
+  // K operand (A of S^T = K Q^T): key row 32*blk + krow(col), columns 16*st + 8*half
+  const int k_off = krow(col) * kKStride + 8 * half;
+  const int k_off_tail = krow(col) * kKStride + 64 + 4 * half;
   // V^T operand (A of O^T = V^T P^T) via transpose reads: this lane names
-  // row 16t + 4*half + ((lane>>2)&3) (+8 for the second read) and column
-  // 32*mt + 16*((lane>>4)&1) + 4*(lane&3); the row-sum tile (mt = 2, D = 72)
-  // reads columns 64 + 4*(lane&3) in both 16-lane groups.
-  const int v_row = 4 * half + ((lane >> 2) & 3);
+  // key row 16t + krow(4*half + ((lane>>2)&3)) (+8 for the second read) and
+  // column 32*mt + 16*((lane>>4)&1) + 4*(lane&3); the row-sum tile (mt = 2,
+  // D = 72) reads columns 64 + 4*(lane&3) in both 16-lane groups.
+  const int v_row = krow(4 * half + ((lane >> 2) & 3));
   const int v_off = v_row * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int v_off_tail = v_row * kVStride + 64 + 4 * (lane & 3);
 
@@ -331,9 +362,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
     return __builtin_bit_cast(bf16x8, w);
   };
-  // s[blk][r] is the logit of key kb + 32*blk + 8*(r/4) + 4*half + (r%4);
+  // s[blk][r] is the logit of key kb + 32*blk + krow(8*(r/4) + 4*half + (r%4));
   // element e = 16*blk + r, and P V step t uses elements 8t .. 8t+7.
-  auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * half + (e & 3); };
+  auto key_of = [&](int e) { return 32 * (e >> 4) + krow(8 * ((e & 15) >> 2) + 4 * half + (e & 3)); };
   // partial row max over elements 4g .. 4g+3
   auto max4 = [&](const f32x16* s, int g) {
     const f32x16& v = s[g >> 2];
