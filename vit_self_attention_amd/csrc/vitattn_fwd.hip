@@ -177,12 +177,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr int kVTile = kBlockN * kVStride;
   constexpr int kStageElems = kKTile + kVTile;
   // LDS ring: tile t lives in stage t % kStages and is fetched kStages-1
-  // tiles ahead of the one being reduced (8-wave workgroups own the whole
-  // LDS of a compute unit and use a deeper ring).
-  constexpr int kStages = NW >= 8 ? 8 : 4;
+  // tiles ahead of the one being reduced; two workgroups share a compute unit.
+  constexpr int kStages = 4;
+  static_assert(NW <= 4, "the LDS ring is sized for two workgroups of at most four waves");
   // Direct-to-LDS fetches: each wave instruction moves 64 lanes x 16 B into
-  // 64 consecutive 16-byte LDS slots.  K uses 9 slots per row, V 9 (D = 64)
-  // or 10 (D = 72); slots past the D values of a row are never fetched.
+  // 64 consecutive 16-byte LDS slots, 9 per K row and 10 per V row.  Slots
+  // past the D values of a row receive a copy of the row's last chunk: they
+  // are never read, except V's slot 9 for D = 72, which is rewritten with
+  // [1, 0, ..., 0] once the tile has landed (write_ones below).
   constexpr int kKSlotsRow = kKStride / 8, kVSlotsRow = kVStride / 8;
   constexpr int kKInstr = kBlockN * kKSlotsRow / 64;
   constexpr int kVInstr = kBlockN * kVSlotsRow / 64;
@@ -213,14 +215,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   const uint16_t* kbase = a.k + b * a.k_sb + h * a.k_sh;
   const uint16_t* vbase = a.v + b * a.v_sb + h * a.v_sh;
 
-  // ---- constant tail of each V row (D = 72): d = 72 holds 1, d = 73..79 hold 0
-  if constexpr (kOnesRow) {
-    for (int r = tid; r < kStages * kBlockN; r += 64 * NW) {
+  // ---- constant tail of each V row (D = 72): d = 72 holds 1, d = 73..79
+  // hold 0.  Every wave writes the whole column of a stage itself (lane =
+  // row) after the stage's tile has landed and before it reads the tile's
+  // V, so no other wave's write needs to be visible to it.
+  auto write_ones = [&](int stage) __attribute__((always_inline)) {
+    if constexpr (kOnesRow) {
       const u32x4 w = {0x3f80u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(
-          &lds[(r / kBlockN) * kStageElems + kKTile + (r % kBlockN) * kVStride + 72]) = w;
+      *reinterpret_cast<u32x4*>(&lds[stage * kStageElems + kKTile + lane * kVStride + 72]) = w;
     }
-  }
+  };
 
   // ---- this lane's query row as the B operand of S^T = K Q^T
   const int q0 = kSplit ? qb * 32 : qb * (32 * NW) + wave * 32;
@@ -248,64 +252,70 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // ---- direct-to-LDS tile fetch.  Fetch instruction i of this wave is
   // number I = i*NW + wave of the tile: I < kKInstr fills K slots, the rest
   // V slots.  Slot s of a row-major LDS tile holds row s / slots_per_row,
-  // 16-byte column s % slots_per_row.  In the last tile, rows past N repeat
-  // row N-1 (finite data that the mask or a zero weight removes).
+  // 16-byte column s % slots_per_row (clamped to the last chunk of D).  In
+  // the last tile, rows past N repeat row N-1 (finite data that a zero
+  // weight removes).
   const int k_st32 = static_cast<int>(a.k_st), v_st32 = static_cast<int>(a.v_st);
   uint32_t f_off[kPerWave];  // byte offset of this lane's chunk from the tile's first row
-  int f_rc[kPerWave];        // row | column << 8; column >= D/8 marks a slot never fetched
+  int f_rc[kPerWave];        // row | clamped column << 8
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
     const int I = i * NW + wave;
     const bool is_k = I < kKInstr;
     const int slot = (is_k ? I : I - kKInstr) * 64 + lane;
     const int per_row = is_k ? kKSlotsRow : kVSlotsRow;
-    const int row = slot / per_row, cc = slot - (slot / per_row) * per_row;
+    const int row = slot / per_row, c0 = slot - (slot / per_row) * per_row;
+    const int cc = c0 < D / 8 ? c0 : D / 8 - 1;
     f_rc[i] = row | (cc << 8);
     f_off[i] = static_cast<uint32_t>((row * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
   }
-  // issues fetch instruction i of tile t (nothing for waves with fewer)
-  auto fetch_one = [&](int t, int i) __attribute__((always_inline)) {
-    const int I = i * NW + wave;
-    if (I >= kInstr) return;
+  // issues this wave's fetch instructions for tile t as straight-line code
+  // (every lane of every instruction fetches; the tail is one uniform branch)
+  auto fetch_tile = [&](int t) __attribute__((always_inline)) {
     const int kb = t * kBlockN;
-    const bool is_k = I < kKInstr;
-    const char* g = is_k ? reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st)
-                         : reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
-    const int dst = (t % kStages) * kStageElems + (is_k ? I * 512 : kKTile + (I - kKInstr) * 512);
-    const int cc = f_rc[i] >> 8;
-    if (cc < D / 8) {
-      uint32_t off = f_off[i];
-      if (kb + kBlockN > N) {
-        const int last = N - 1 - kb;
-        const int row = f_rc[i] & 255;
-        const int r = row < last ? row : last;
-        off = static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
+    const char* gk = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st);
+    const char* gv = reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
+    const uint32_t stage = lds_base + 2 * (t % kStages) * kStageElems;
+    auto slot_addr = [&](int I) {
+      return stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512);
+    };
+    if (kb + kBlockN <= N) {
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int I = i * NW + wave;
+        if (i >= kMinPerWave && I >= kInstr) continue;  // only the last round can be short
+        dma16(I < kKInstr ? gk : gv, f_off[i], slot_addr(I));
       }
-      dma16(g, off, lds_base + 2 * dst);
+    } else {
+      const int last = N - 1 - kb;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int I = i * NW + wave;
+        if (i >= kMinPerWave && I >= kInstr) continue;
+        const bool is_k = I < kKInstr;
+        const int row = f_rc[i] & 255, cc = f_rc[i] >> 8;
+        const int r = row < last ? row : last;
+        dma16(is_k ? gk : gv, static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2), slot_addr(I));
+      }
     }
   };
-  auto fetch_tile = [&](int t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) fetch_one(t, i);
-  };
-  // Waits until at most `n` fetch instructions of this wave are in flight
-  // (vector-memory counter; the other counters are left alone), then meets
-  // the rest of the workgroup.  The memory clobber keeps LDS reads after it.
+  // Waits until the fetches of all but the last `tiles_in_flight` (0 or 1)
+  // tiles issued by this wave have landed (vector-memory counter only; a
+  // wave issues at least kMinPerWave fetches per tile), then meets the rest
+  // of the workgroup.  The memory clobber keeps LDS accesses after it.
   auto wait_fetch_and_sync = [&](int tiles_in_flight) __attribute__((always_inline)) {
     // vmcnt(n) only (expcnt 7, lgkmcnt 15 mean "no wait" for those counters)
 #define VITATTN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-    switch (tiles_in_flight) {
-      case 0: VITATTN_WAIT_VM(0); break;
-      case 1: VITATTN_WAIT_VM(kMinPerWave); break;
-      case 2: VITATTN_WAIT_VM(2 * kMinPerWave); break;
-      case 3: VITATTN_WAIT_VM(3 * kMinPerWave); break;
-      case 4: VITATTN_WAIT_VM(4 * kMinPerWave); break;
-      default: VITATTN_WAIT_VM(5 * kMinPerWave); break;
+    if (tiles_in_flight == 0) {
+      VITATTN_WAIT_VM(0);
+    } else {
+      VITATTN_WAIT_VM(kMinPerWave);
     }
 #undef VITATTN_WAIT_VM
     asm volatile("s_barrier" ::: "memory");
   };
-  // tiles fetched after tile t, at the point where the fetch of tile `issued` is the last one
+  // tiles fetched after tile t (0 or 1 with a four-stage ring), at the point
+  // where the fetch of tile `issued` is the last one
   auto after = [&](int t, int issued) { return issued > t ? issued - t : 0; };
 
   // ---- key order.  Row i of each 32-key block of S^T holds key
@@ -404,6 +414,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     // last barrier; it is refilled with tile j + kStages - 1
     const int tf = j + kStages - 1;
     if (!kSplit && tf < ntiles) fetch_tile(tf);
+    // tile j+1 landed before the last barrier; its V is read in the next step
+    if (!kSplit && j + 1 < ntiles) write_ones((j + 1) % kStages);
 
     if (wave_active) {
       // lazy running max: move it (and rescale) only when some row's max
@@ -524,10 +536,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 #pragma unroll
     for (int t = 0; t < kStages; ++t)
       if (t < ntiles) fetch_tile(t);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // the V ones column (LDS stores) is written
     wait_fetch_and_sync(0);
     const int my = wave;
     if (wave_active && my < ntiles) {
+      write_ones(my);
       qk_plain(lds + my * kStageElems, sa);
       mx = rowmax(sa);
       if (ragged && my == ntiles - 1) step(my, sa, sb, False{}, True{});
@@ -599,9 +611,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
     if (t < ntiles) fetch_tile(t);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // the V ones column (LDS stores) is written
   // tiles 0 and 1 have landed
   wait_fetch_and_sync(after(1, (kStages - 2 < ntiles - 1 ? kStages - 2 : ntiles - 1)));
+  write_ones(0);
 
   if (wave_active) {
     qk_plain(lds, sa);
