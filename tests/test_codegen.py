@@ -59,7 +59,7 @@ def test_m0_is_only_written_by_the_fetch_sequence(asm):
             if "m0" not in ln:
                 continue
             # the only instruction that names m0 is the asm's own write ...
-            assert re.match(r"s_mov_b32 m0, s\d+$", ln), (name, ln)
+            assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", ln), (name, ln)
             # ... followed by the wait state and the fetch that reads it
             assert body[i + 1] == "s_nop 0", (name, body[i:i + 3])
             assert body[i + 2].startswith("global_load_lds_dwordx4"), (name, body[i:i + 3])

@@ -76,7 +76,8 @@ struct KernelArgs {
   int64_t o_sb, o_sh, o_st;
   int H, N;
   int qblocks;     // query blocks per (image, head)
-  int grid;        // total workgroups
+  int items;       // B * H * qblocks work items (image, head, query block)
+  int grid;        // total workgroups: one per item, or fewer that loop over items
   float c;         // max(|scale|, tiny) * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0: Q is negated instead
 };
@@ -193,7 +194,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr int kMinPerWave = kInstr / NW;           // ... and of the least busy one
   static_assert(kBlockN * kKSlotsRow % 64 == 0 && kBlockN * kVSlotsRow % 64 == 0, "slots");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems];
+  // the ring, then a 1 KB sink that touch_q's fetches land in (never read)
+  constexpr int kSinkElems = 512;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems + kSinkElems];
   // byte address of lds in the LDS aperture (what M0 takes)
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint16_t*)lds));
@@ -204,14 +207,36 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   const int col = lane & 31;   // query within the wave (MFMA column)
   const int half = lane >> 5;  // which half of the MFMA K dimension this lane feeds
 
-  const int tile_id = xcd_remap(blockIdx.x, a.grid);
-  const int bh = tile_id / a.qblocks;
-  const int qb = tile_id - bh * a.qblocks;
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
   const int N = a.N;
   const int ntiles = (N + kBlockN - 1) / kBlockN;
 
+  // ---- work items.  With one workgroup per item, item = xcd_remap(block).
+  // With fewer workgroups (a whole number per XCD), each loops over items:
+  // XCD x owns a contiguous range of items and its workgroups take them in
+  // turn, so the query blocks of one (image, head), which read the same K
+  // and V, run at about the same time in that XCD's L2.
+  int it0, istep, iend;
+  if (a.grid >= a.items) {
+    it0 = xcd_remap(blockIdx.x, a.grid);
+    istep = 1;
+    iend = it0 + 1;
+  } else {
+    const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
+    const int per = a.items >> 3, rem = a.items & 7;
+    const int lo = x * per + (x < rem ? x : rem);
+    it0 = lo + l;
+    istep = a.grid >> 3;
+    iend = lo + per + (x < rem ? 1 : 0);
+  }
+  const int nitems = it0 < iend ? (iend - it0 + istep - 1) / istep : 0;
+  auto coords = [&](int item, int& bi, int& hi, int& qbi) {
+    const int bh = item / a.qblocks;
+    qbi = item - bh * a.qblocks;
+    bi = bh / a.H;
+    hi = bh - bi * a.H;
+  };
+  int b, h, qb;
+  coords(it0, b, h, qb);
   const uint16_t* kbase = a.k + b * a.k_sb + h * a.k_sh;
   const uint16_t* vbase = a.v + b * a.v_sb + h * a.v_sh;
 
@@ -227,27 +252,44 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   };
 
   // ---- this lane's query row as the B operand of S^T = K Q^T
-  const int q0 = kSplit ? qb * 32 : qb * (32 * NW) + wave * 32;
-  const int qi = q0 + col;
-  const bool wave_active = q0 < N;
+  auto first_query = [&](int qb_) { return kSplit ? qb_ * 32 : qb_ * (32 * NW) + wave * 32; };
+  // loads the query row of this lane for item (b_, h_, qb_) into dq, dqt as
+  // stored (rows past N load row N-1: their columns of S are never stored
+  // and touch no other column); sign_q then applies the sign of the scale
+  auto load_q = [&](int b_, int h_, int qb_, bf16x8* dq, bf16x4& dqt) __attribute__((always_inline)) {
+    const int q_ = first_query(qb_) + col;
+    const int qi_ = q_ < N ? q_ : N - 1;
+    const uint16_t* qrow = a.q + b_ * a.q_sb + h_ * a.q_sh + static_cast<int64_t>(qi_) * a.q_st;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dq[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
+    if constexpr (D == 72) dqt = *reinterpret_cast<const bf16x4*>(qrow + 64 + 4 * half);
+  };
+  auto sign_q = [&](bf16x8* dq, bf16x4& dqt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dq[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, dq[s]) ^ a.qsign);
+    if constexpr (D == 72) dqt = __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, dqt) ^ a.qsign);
+  };
+  int q0 = first_query(qb);
+  int qi = q0 + col;
+  bool wave_active = q0 < N;
   bf16x8 qf[4];
   bf16x4 qt = {};
-  {
-    const uint16_t* qrow = a.q + b * a.q_sb + h * a.q_sh + static_cast<int64_t>(qi) * a.q_st;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (qi < N) w = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half);
-      w ^= a.qsign;
-      qf[s] = __builtin_bit_cast(bf16x8, w);
-    }
-    if constexpr (D == 72) {
-      u32x2 w = {0u, 0u};
-      if (qi < N) w = *reinterpret_cast<const u32x2*>(qrow + 64 + 4 * half);
-      w ^= a.qsign;
-      qt = __builtin_bit_cast(bf16x4, w);
-    }
-  }
+  load_q(b, h, qb, qf, qt);
+  sign_q(qf, qt);
+  int nb = b, nh = h, nqb = qb;  // next item (the current one after the last)
+  // Brings the next item's query rows of this wave into the caches, ahead
+  // of load_q: one direct-to-LDS fetch of each row's
+  // first and last 16-byte chunks (every cache line a row of 2*D <= 144
+  // bytes touches), landing in the LDS sink.
+  auto touch_q = [&]() __attribute__((always_inline)) {
+    const int qn0 = first_query(nqb);
+    const int qlo = qn0 < N ? qn0 : N - 1;
+    const int r = qn0 + col < N ? qn0 + col : N - 1;
+    const char* base = reinterpret_cast<const char*>(a.q + nb * a.q_sb + nh * a.q_sh +
+                                                     static_cast<int64_t>(qlo) * a.q_st);
+    const uint32_t off = static_cast<uint32_t>((r - qlo) * a.q_st * 2 + (2 * D - 16) * half);
+    dma16(base, off, lds_base + 2 * kStages * kStageElems);
+  };
 
   // ---- direct-to-LDS tile fetch.  Fetch instruction i of this wave is
   // number I = i*NW + wave of the tile: I < kKInstr fills K slots, the rest
@@ -256,26 +298,33 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // the last tile, rows past N repeat row N-1 (finite data that a zero
   // weight removes).
   const int k_st32 = static_cast<int>(a.k_st), v_st32 = static_cast<int>(a.v_st);
-  uint32_t f_off[kPerWave];  // byte offset of this lane's chunk from the tile's first row
-  int f_rc[kPerWave];        // row | clamped column << 8
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int I = i * NW + wave;
+  // row and clamped 16-byte column of this lane's slot in fetch instruction I
+  auto slot_rc = [&](int I, int& row, int& cc) __attribute__((always_inline)) {
     const bool is_k = I < kKInstr;
     const int slot = (is_k ? I : I - kKInstr) * 64 + lane;
     const int per_row = is_k ? kKSlotsRow : kVSlotsRow;
-    const int row = slot / per_row, c0 = slot - (slot / per_row) * per_row;
-    const int cc = c0 < D / 8 ? c0 : D / 8 - 1;
-    f_rc[i] = row | (cc << 8);
-    f_off[i] = static_cast<uint32_t>((row * (is_k ? k_st32 : v_st32) + cc * 8) * 2);
+    row = slot / per_row;
+    const int c0 = slot - row * per_row;
+    cc = c0 < D / 8 ? c0 : D / 8 - 1;
+  };
+  uint32_t f_off[kPerWave];  // byte offset of this lane's chunk from the tile's first row
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int I = i * NW + wave;
+    int row, cc;
+    slot_rc(I, row, cc);
+    f_off[i] = static_cast<uint32_t>((row * (I < kKInstr ? k_st32 : v_st32) + cc * 8) * 2);
   }
-  // issues this wave's fetch instructions for tile t as straight-line code
-  // (every lane of every instruction fetches; the tail is one uniform branch)
-  auto fetch_tile = [&](int t) __attribute__((always_inline)) {
+  // issues this wave's fetch instructions for key tile t of the (image,
+  // head) whose K and V start at kb_ptr and vb_ptr, into LDS stage `st`, as
+  // straight-line code (every lane of every instruction fetches; the tail
+  // is one uniform branch)
+  auto fetch_tile_at = [&](const uint16_t* kb_ptr, const uint16_t* vb_ptr, int t, int st)
+                           __attribute__((always_inline)) {
     const int kb = t * kBlockN;
-    const char* gk = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb) * a.k_st);
-    const char* gv = reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb) * a.v_st);
-    const uint32_t stage = lds_base + 2 * (t % kStages) * kStageElems;
+    const char* gk = reinterpret_cast<const char*>(kb_ptr + static_cast<int64_t>(kb) * a.k_st);
+    const char* gv = reinterpret_cast<const char*>(vb_ptr + static_cast<int64_t>(kb) * a.v_st);
+    const uint32_t stage = lds_base + 2 * st * kStageElems;
     auto slot_addr = [&](int I) {
       return stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512);
     };
@@ -293,27 +342,53 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         const int I = i * NW + wave;
         if (i >= kMinPerWave && I >= kInstr) continue;
         const bool is_k = I < kKInstr;
-        const int row = f_rc[i] & 255, cc = f_rc[i] >> 8;
+        int row, cc;
+        slot_rc(I, row, cc);
         const int r = row < last ? row : last;
         dma16(is_k ? gk : gv, static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2), slot_addr(I));
       }
     }
   };
+  // ---- the tile stream.  The workgroup reduces the key tiles of its items
+  // one after another; stream tile s (tile s % ntiles of the workgroup's
+  // item s / ntiles) lives in LDS stage s % kStages and is fetched
+  // kStages-1 tiles ahead, across item boundaries.
+  const int stream_len = nitems * ntiles;
+  int f_s = 0, f_t = 0, f_item = it0;  // next stream tile to fetch
+  const uint16_t* f_kb = kbase;
+  const uint16_t* f_vb = vbase;
+  auto fetch_next = [&]() __attribute__((always_inline)) {
+    if (f_s >= stream_len) return;
+    fetch_tile_at(f_kb, f_vb, f_t, f_s % kStages);
+    ++f_s;
+    if (++f_t == ntiles && f_s < stream_len) {
+      f_t = 0;
+      f_item += istep;
+      int bn, hn, qn;
+      coords(f_item, bn, hn, qn);
+      f_kb = a.k + bn * a.k_sb + hn * a.k_sh;
+      f_vb = a.v + bn * a.v_sb + hn * a.v_sh;
+    }
+  };
   // Waits until the fetches of all but the last `tiles_in_flight` (0 or 1)
   // tiles issued by this wave have landed (vector-memory counter only; a
-  // wave issues at least kMinPerWave fetches per tile), then meets the rest
-  // of the workgroup.  The memory clobber keeps LDS accesses after it.
-  auto wait_fetch_and_sync = [&](int tiles_in_flight) __attribute__((always_inline)) {
+  // wave issues at least kMinPerWave fetches per tile, and kLater other
+  // loads after them), then meets the rest of the workgroup.  The memory
+  // clobber keeps LDS accesses after it.
+  auto wait_fetch_and_sync = [&](int tiles_in_flight, auto kLaterC) __attribute__((always_inline)) {
+    constexpr int kLater = decltype(kLaterC)::value;
+    asm volatile("" ::: "memory");  // the later loads stay ahead of the count
     // vmcnt(n) only (expcnt 7, lgkmcnt 15 mean "no wait" for those counters)
 #define VITATTN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
     if (tiles_in_flight == 0) {
-      VITATTN_WAIT_VM(0);
+      VITATTN_WAIT_VM(kLater);
     } else {
-      VITATTN_WAIT_VM(kMinPerWave);
+      VITATTN_WAIT_VM(kMinPerWave + kLater);
     }
 #undef VITATTN_WAIT_VM
     asm volatile("s_barrier" ::: "memory");
   };
+  using NoLater = std::integral_constant<int, 0>;
   // tiles fetched after tile t (0 or 1 with a four-stage ring), at the point
   // where the fetch of tile `issued` is the last one
   auto after = [&](int t, int issued) { return issued > t ? issued - t : 0; };
@@ -407,15 +482,23 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // one MFMA with the LDS reads of the MFMA two steps later and a share of
   // the VALU work (exponentials, bf16 packing, maxima), so the VALU runs
   // while the matrix core works.
-  auto step = [&](int j, f32x16* cur, f32x16* nxt, auto kNextC, auto kRaggedC) __attribute__((always_inline)) {
+  // j is the tile's index in its item, gs its index in the tile stream
+  // (gs = j for the split kernel, whose stage of tile j is stage j).
+  auto step = [&](int j, int gs, f32x16* cur, f32x16* nxt, auto kNextC, auto kRaggedC)
+                  __attribute__((always_inline)) {
     constexpr bool kNext = decltype(kNextC)::value;
     constexpr bool kRagged = decltype(kRaggedC)::value;
-    // stage (j-1) % kStages held tile j-1, whose reads all ended before the
-    // last barrier; it is refilled with tile j + kStages - 1
-    const int tf = j + kStages - 1;
-    if (!kSplit && tf < ntiles) fetch_tile(tf);
-    // tile j+1 landed before the last barrier; its V is read in the next step
-    if (!kSplit && j + 1 < ntiles) write_ones((j + 1) % kStages);
+    if constexpr (!kSplit) {
+      // stage (gs-1) % kStages held stream tile gs-1, whose reads all ended
+      // before the last barrier; it is refilled with stream tile gs + kStages - 1
+      fetch_next();
+      // three steps before the item ends: touch the next item's query rows.
+      // Issued after this step's fetches, it has two steps to land: the
+      // wait at the end of this step leaves it in flight, the next one not.
+      if (kNext && j == ntiles - 3 && gs + 3 < stream_len) touch_q();
+      // stream tile gs+1 landed before the last barrier; its V is read next step
+      if (gs + 1 < stream_len) write_ones((gs + 1) % kStages);
+    }
 
     if (wave_active) {
       // lazy running max: move it (and rescale) only when some row's max
@@ -433,8 +516,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       }
       const float neg_m = -m_run;
       const int kb = j * kBlockN;
-      const uint16_t* kt = lds + ((j + 1) % kStages) * kStageElems;
-      const uint16_t* vt = lds + (j % kStages) * kStageElems + kKTile;
+      const uint16_t* kt = lds + ((gs + 1) % kStages) * kStageElems;
+      const uint16_t* vt = lds + (gs % kStages) * kStageElems + kKTile;
 
       float p[32];
       uint32_t w[16];
@@ -492,7 +575,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       bf16x8 vo[kPv];
       vo[0] = v_read(vt, 0);
       vo[1] = v_read(vt, 1);
-      float gm[8];
+      float gmax = -__builtin_inff();  // running max of the logits of tile j+1
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kPv; ++i) {
@@ -505,13 +588,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         } else if constexpr (kNext) {
           const int ii = i - kHalfPv;
 #pragma unroll
-          for (int g = 8 * ii / kHalfPv; g < 8 * (ii + 1) / kHalfPv; ++g) gm[g] = max4(nxt, g);
+          for (int g = 8 * ii / kHalfPv; g < 8 * (ii + 1) / kHalfPv; ++g) gmax = fmaxf(gmax, max4(nxt, g));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (kNext) {
-        mx = max_across_halves(fmaxf(fmaxf(fmaxf(gm[0], gm[1]), fmaxf(gm[2], gm[3])),
-                                     fmaxf(fmaxf(gm[4], gm[5]), fmaxf(gm[6], gm[7]))));
+        mx = max_across_halves(gmax);
       }
       if constexpr (!kOnesRow) {
         l_run += psum;
@@ -519,10 +601,29 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       }
     }
 
-    // tile j+2 must have landed before the next step reads its K
-    if constexpr (kNext) {
-      const int last_issued = (j + kStages - 1 < ntiles ? j + kStages - 1 : ntiles - 1);
-      wait_fetch_and_sync(after(j + 2, last_issued));
+    if constexpr (!kSplit && !kNext) {
+      // the item's last tile is reduced: start loading the next item's query
+      // rows into qf, qt (after the last item this reloads that item's rows,
+      // which are not used again)
+      load_q(nb, nh, nqb, qf, qt);
+    }
+    // stream tile gs+2 must have landed before the next step reads its K,
+    // and every wave must be done with stage gs % kStages before it is refilled
+    if constexpr (!kSplit) {
+      if constexpr (kNext) {
+        if (j == ntiles - 3 && gs + 3 < stream_len) {
+          wait_fetch_and_sync(after(gs + 2, f_s - 1), std::integral_constant<int, 1>{});
+        } else if (gs + 1 < stream_len) {
+          wait_fetch_and_sync(after(gs + 2, f_s - 1), NoLater{});
+        }
+      } else {
+        // Everything this wave has in flight, the next item's query rows
+        // included, lands here (its last fetch was issued a step ago): the
+        // compiler's own waits for those rows then find nothing left to wait
+        // for in the next item, where a count of its loads alone would also
+        // wait for fetches issued after them.
+        wait_fetch_and_sync(0, NoLater{});
+      }
     }
   };
 
@@ -535,15 +636,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     // ---- all tiles (at most kStages) in LDS at once; wave w reduces tile w
 #pragma unroll
     for (int t = 0; t < kStages; ++t)
-      if (t < ntiles) fetch_tile(t);
-    wait_fetch_and_sync(0);
+      if (t < ntiles) fetch_tile_at(kbase, vbase, t, t);
+    wait_fetch_and_sync(0, NoLater{});
     const int my = wave;
     if (wave_active && my < ntiles) {
       write_ones(my);
       qk_plain(lds + my * kStageElems, sa);
       mx = rowmax(sa);
-      if (ragged && my == ntiles - 1) step(my, sa, sb, False{}, True{});
-      else step(my, sa, sb, False{}, False{});
+      if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{});
+      else step(my, my, sa, sb, False{}, False{});
     }
     // ---- merge the partial results of the waves (each: running max m,
     // accumulator, and for D = 64 the partial row sum) through LDS, laid out
@@ -605,59 +706,100 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     return;
   }
 
-  // ---- prologue: fetch tiles 0..2; S_0 and its row max in registers.
-  // Keys past N in the last tile hold copies of key N-1 (see fetch_tile),
-  // which leave every row max unchanged; only their weights are zeroed.
+  // ---- prologue: fetch stream tiles 0..2 and wait for tiles 0 and 1.
+  // Keys past N in an item's last tile hold copies of key N-1 (see
+  // fetch_tile_at), which leave every row max unchanged; only their weights
+  // are zeroed.
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
-    if (t < ntiles) fetch_tile(t);
-  // tiles 0 and 1 have landed
-  wait_fetch_and_sync(after(1, (kStages - 2 < ntiles - 1 ? kStages - 2 : ntiles - 1)));
+  for (int t = 0; t < kStages - 1; ++t) fetch_next();
+  wait_fetch_and_sync(after(1, f_s - 1), NoLater{});
   write_ones(0);
 
-  if (wave_active) {
-    qk_plain(lds, sa);
-    mx = rowmax(sa);
-  }
-  int j = 0;
-  for (; j + 2 < ntiles; j += 2) {
-    step(j, sa, sb, True{}, False{});
-    step(j + 1, sb, sa, True{}, False{});
-  }
-  if (j + 1 < ntiles) {
-    step(j, sa, sb, True{}, False{});
-    if (ragged) step(j + 1, sb, sa, False{}, True{});
-    else step(j + 1, sb, sa, False{}, False{});
-  } else {
-    if (ragged) step(j, sa, sb, False{}, True{});
-    else step(j, sa, sb, False{}, False{});
-  }
-
-  if (!wave_active) return;
-
-  // ---- epilogue: O = acc / l, bf16, rows < N only
-  float l;
-  if constexpr (kOnesRow) {
-    // row D sits in output tile 2, register 4, of the lanes with half == 0
-    l = lower_half_value(acc[2][4]);
-  } else {
-    l = sum_across_halves(l_run);
-  }
-  const float inv = 1.0f / l;
-  if (qi < N) {
-    uint16_t* orow = a.o + b * a.o_sb + h * a.o_sh + static_cast<int64_t>(qi) * a.o_st;
+  int g0 = 0;  // stream index of the current item's tile 0
+  for (int m = 0; m < nitems; ++m, g0 += ntiles) {
+    if (m > 0) {
+      b = nb;
+      h = nh;
+      qb = nqb;
+      q0 = first_query(qb);
+      qi = q0 + col;
+      wave_active = q0 < N;
+      sign_q(qf, qt);  // loaded during the previous item's last step
 #pragma unroll
-    for (int mt = 0; mt < kOutTiles; ++mt)
+      for (int t = 0; t < kOutTiles; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * mt + 8 * g + 4 * half;
-        if (d0 < D) {
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[mt][4 * g + 0] * inv, acc[mt][4 * g + 1] * inv);
-          w[1] = pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+      m_run = -__builtin_inff();
+      l_run = 0.f;
+    }
+    if (m + 1 < nitems) coords(it0 + (m + 1) * istep, nb, nh, nqb);
+    // S_0 of the item and its row max in registers (stream tile g0 landed
+    // before the last barrier)
+    if (wave_active) {
+      qk_plain(lds + (g0 % kStages) * kStageElems, sa);
+      mx = rowmax(sa);
+    }
+    int j = 0;
+    for (; j + 2 < ntiles; j += 2) {
+      step(j, g0 + j, sa, sb, True{}, False{});
+      step(j + 1, g0 + j + 1, sb, sa, True{}, False{});
+    }
+    if (j + 1 < ntiles) {
+      step(j, g0 + j, sa, sb, True{}, False{});
+      if (ragged) step(j + 1, g0 + j + 1, sb, sa, False{}, True{});
+      else step(j + 1, g0 + j + 1, sb, sa, False{}, False{});
+    } else {
+      if (ragged) step(j, g0 + j, sa, sb, False{}, True{});
+      else step(j, g0 + j, sa, sb, False{}, False{});
+    }
+
+    // ---- epilogue: O = acc / l in bf16, rows < N only.  The tile goes
+    // through the LDS stage of the item's last key tile (free until the next
+    // step refills it), so that each global store writes 16 contiguous bytes
+    // of a row and consecutive lanes write consecutive bytes of the rows.
+    {
+      constexpr int kOS = 72;  // row stride of the staged tile (elements)
+      static_assert(NW * 32 * kOS <= kStageElems, "staged output tile must fit in a stage");
+      uint16_t* ob = lds + ((g0 + ntiles - 1) % kStages) * kStageElems + wave * 32 * kOS;
+      if (wave_active) {
+        float l;
+        if constexpr (kOnesRow) {
+          // row D sits in output tile 2, register 4, of the lanes with half == 0
+          l = lower_half_value(acc[2][4]);
+        } else {
+          l = sum_across_halves(l_run);
+        }
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int mt = 0; mt < kOutTiles; ++mt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = 32 * mt + 8 * g + 4 * half;
+            if (d0 < D) {
+              u32x2 w;
+              w[0] = pack_bf16x2(acc[mt][4 * g + 0] * inv, acc[mt][4 * g + 1] * inv);
+              w[1] = pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv);
+              *reinterpret_cast<u32x2*>(ob + col * kOS + d0) = w;
+            }
+          }
+        // store k covers rows kRows*k .. kRows*k + kRows-1: lane l writes
+        // 16-byte chunk l % (D/8) of row kRows*k + l / (D/8)
+        constexpr int kRowChunks = D / 8, kRows = 64 / kRowChunks;
+        const int r0 = lane / kRowChunks, ch = lane - r0 * kRowChunks;
+        const uint16_t* src = ob + r0 * kOS + 8 * ch;
+        uint16_t* dst = a.o + b * a.o_sb + h * a.o_sh + static_cast<int64_t>(q0 + r0) * a.o_st + 8 * ch;
+        const int64_t dst_step = static_cast<int64_t>(kRows) * a.o_st;
+#pragma unroll
+        for (int k = 0; k < (32 + kRows - 1) / kRows; ++k) {
+          const int row = kRows * k + r0;
+          if (r0 < kRows && row < 32 && q0 + row < N)
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src + kRows * k * kOS);
+          dst += dst_step;
         }
       }
+      // every wave is done with the stage before the next step refills it
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   }
 }
 
@@ -665,6 +807,22 @@ template <int D, int NW, bool kSplit>
 int launch(const KernelArgs& ka, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka);
   return hipGetLastError() == hipSuccess ? VITATTN_OK : VITATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+namespace {
+
+// compute units of the current device (0 if unknown), cached per device
+int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  static int cache[64] = {0};
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 }  // namespace
@@ -704,7 +862,15 @@ int launch_fwd(const FwdArgs& f, void* stream) {
   const int nw = pick_waves(f.B, f.H, f.N);
   const int qpb = nw < 0 ? 32 : 32 * nw;  // queries per workgroup
   ka.qblocks = (f.N + qpb - 1) / qpb;
-  ka.grid = f.B * f.H * ka.qblocks;
+  ka.items = f.B * f.H * ka.qblocks;
+  ka.grid = ka.items;
+  if (nw == 4) {
+    // Two four-wave workgroups fit on a compute unit.  With more items than
+    // that, exactly that many workgroups loop over the items, fetching the
+    // next item's key tiles while they finish the current one.
+    const int slots = 2 * compute_units();
+    if (slots > 0 && slots % 8 == 0 && ka.items > slots) ka.grid = slots;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (f.D == 64) {
     if (nw == -4) return launch<64, 4, true>(ka, s);
