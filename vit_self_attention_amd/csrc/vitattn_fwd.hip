@@ -211,24 +211,43 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   const int ntiles = (N + kBlockN - 1) / kBlockN;
 
   // ---- work items.  With one workgroup per item, item = xcd_remap(block).
-  // With fewer workgroups (a whole number per XCD), each loops over items:
-  // XCD x owns a contiguous range of items and its workgroups take them in
-  // turn, so the query blocks of one (image, head), which read the same K
-  // and V, run at about the same time in that XCD's L2.
-  int it0, istep, iend;
+  // With fewer workgroups (two per compute unit, a whole number per XCD),
+  // each loops over items in rounds: XCD x owns a contiguous range of items
+  // and round r gives its workgroup l the item lo + r*G + l, so the query
+  // blocks of one (image, head), which read the same K and V, run at about
+  // the same time in that XCD's L2.  Of the two workgroups on a compute
+  // unit, the one dispatched first (block < grid/2) wins most issue
+  // conflicts and runs about 1.2 times faster: the last rounds, past
+  // 0.9 times the average number of items, go to those workgroups only.
+  // (The host loops only with at least two items per workgroup.)
+  int it0 = 0, lo = 0, hi = 0, gx = 1, ky = 1, lx = 0;
+  bool single = true;
+  int nitems = 1;
   if (a.grid >= a.items) {
     it0 = xcd_remap(blockIdx.x, a.grid);
-    istep = 1;
-    iend = it0 + 1;
   } else {
-    const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
+    single = false;
+    const int x = blockIdx.x & 7;
+    lx = blockIdx.x >> 3;
+    gx = a.grid >> 3;
     const int per = a.items >> 3, rem = a.items & 7;
-    const int lo = x * per + (x < rem ? x : rem);
-    it0 = lo + l;
-    istep = a.grid >> 3;
-    iend = lo + per + (x < rem ? 1 : 0);
+    lo = x * per + (x < rem ? x : rem);
+    const int nx = per + (x < rem ? 1 : 0);
+    hi = lo + nx;
+    ky = (9 * nx + 5 * gx) / (10 * gx);  // 0.9 * nx / gx, rounded, at most nx / gx
+    if (ky > nx / gx) ky = nx / gx;
+    it0 = lo + lx;
+    nitems = ky;
+    if (lx < gx / 2) {
+      const int left = nx - ky * gx - lx;
+      nitems += left > 0 ? (left + gx / 2 - 1) / (gx / 2) : 0;
+    }
   }
-  const int nitems = it0 < iend ? (iend - it0 + istep - 1) / istep : 0;
+  // item of round r
+  auto item_at = [&](int r) {
+    if (single) return it0;
+    return r < ky ? lo + r * gx + lx : lo + ky * gx + (r - ky) * (gx / 2) + lx;
+  };
   auto coords = [&](int item, int& bi, int& hi, int& qbi) {
     const int bh = item / a.qblocks;
     qbi = item - bh * a.qblocks;
@@ -354,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // item s / ntiles) lives in LDS stage s % kStages and is fetched
   // kStages-1 tiles ahead, across item boundaries.
   const int stream_len = nitems * ntiles;
-  int f_s = 0, f_t = 0, f_item = it0;  // next stream tile to fetch
+  int f_s = 0, f_t = 0, f_r = 0;  // next stream tile to fetch: tile f_t of round f_r
   const uint16_t* f_kb = kbase;
   const uint16_t* f_vb = vbase;
   auto fetch_next = [&]() __attribute__((always_inline)) {
@@ -363,9 +382,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     ++f_s;
     if (++f_t == ntiles && f_s < stream_len) {
       f_t = 0;
-      f_item += istep;
+      ++f_r;
       int bn, hn, qn;
-      coords(f_item, bn, hn, qn);
+      coords(item_at(f_r), bn, hn, qn);
       f_kb = a.k + bn * a.k_sb + hn * a.k_sh;
       f_vb = a.v + bn * a.v_sb + hn * a.v_sh;
     }
@@ -732,7 +751,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       m_run = -__builtin_inff();
       l_run = 0.f;
     }
-    if (m + 1 < nitems) coords(it0 + (m + 1) * istep, nb, nh, nqb);
+    if (m + 1 < nitems) coords(item_at(m + 1), nb, nh, nqb);
     // S_0 of the item and its row max in registers (stream tile g0 landed
     // before the last barrier)
     if (wave_active) {
@@ -869,7 +888,7 @@ int launch_fwd(const FwdArgs& f, void* stream) {
     // that, exactly that many workgroups loop over the items, fetching the
     // next item's key tiles while they finish the current one.
     const int slots = 2 * compute_units();
-    if (slots > 0 && slots % 8 == 0 && ka.items > slots) ka.grid = slots;
+    if (slots >= 16 && slots % 8 == 0 && ka.items >= 2 * slots) ka.grid = slots;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (f.D == 64) {
