@@ -6,13 +6,22 @@ for the default workload, SigLIP-So400m/14 at 224 px with two views
 (B=2, N=256, H=16, D=72, packed QKV), that is 27 back-to-back layer calls.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+    python bench.py --sweep        # every workload: trimmed per-layer statistics
 
 Prints ONE JSON line.  `value` is TFLOP/s over the timed steps (algorithmic
 flops 4*B*H*N^2*D per layer call).  Also reported: us per layer call, the
 roofline of the kernel (HIP events on the launch stream),
 the fp64 CPU oracle timed on this host as a baseline, parity of the timed
 outputs with that oracle, and the same figures for the 384 px SigLIP
-workload (B=48, N=729), where the kernel is compute-bound.
+workload (B=48, N=729), where the kernel is compute-bound, and the step
+launched as one recorded HIP graph (a plan) instead of call by call.
+
+--sweep prints one JSON line with, for every workload: 50 samples of its L
+back-to-back layer calls (after 3 warmup passes), the median, 5th and 95th
+percentile of the sample time per layer over the middle 90% of the samples,
+TFLOP/s, % of the bf16 MFMA peak, algorithmic GB/s, the same via a plan, and
+parity of every layer with the fp64 oracle; plus the back-to-back launch
+floor of a one-element kernel.
 """
 from __future__ import annotations
 
@@ -43,6 +52,9 @@ def _parse():
                    help="skip the 384 px SigLIP (B=48, N=729) figures")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline")
+    p.add_argument("--sweep", action="store_true",
+                   help="per-workload statistics for all workloads (one JSON line)")
+    p.add_argument("--samples", type=int, default=50, help="samples per workload in --sweep")
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times "
                         "(reference for HBM byte counters) and exit")
@@ -141,6 +153,101 @@ def _time_steps(va, wl, ins, outs, steps, warmup, stream):
     return t_start.elapsed_time(t_end), time.perf_counter() - wall0
 
 
+def _time_plan(plan, steps, warmup, stream):
+    """As _time_steps, with each step one launch of a recorded plan."""
+    import torch
+
+    for _ in range(warmup):
+        plan.launch(stream)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(steps):
+        plan.launch(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end)
+
+
+def _launch_floor(stream, n=2000):
+    """Back-to-back launch time of a one-element kernel (us per launch)."""
+    import torch
+
+    x = torch.zeros(1, device="cuda:0")
+    for _ in range(50):
+        x.add_(1.0)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(n):
+        x.add_(1.0)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / n
+
+
+def _trimmed(samples):
+    """Median, 5th and 95th percentile over the middle 90% of the samples."""
+    import numpy as np
+
+    xs = np.sort(np.asarray(samples, dtype=np.float64))
+    cut = int(round(0.05 * len(xs)))
+    mid = xs[cut:len(xs) - cut] if len(xs) - 2 * cut > 0 else xs
+    return float(np.median(mid)), float(np.percentile(mid, 5)), float(np.percentile(mid, 95))
+
+
+def _sweep(args):
+    """Per-workload statistics of every workload (the measurement protocol:
+    warm up with 3 passes, 50 samples of the L-layer sequence, trim the top
+    and bottom 5%, report the median and the spread)."""
+    import numpy as np
+    import torch
+    import oracle
+    import vit_self_attention_amd as va
+    from workloads import WORKLOADS
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    stream = torch.cuda.current_stream(device)
+    oracle.set_threads(min(len(os.sched_getaffinity(0)), 16))
+    out = {"metric": "vision-attn fwd us/layer per workload (median of trimmed samples)",
+           "launch_floor_us": _launch_floor(stream), "workloads": {}}
+    for key in sorted(WORKLOADS):
+        wl = WORKLOADS[key]
+        print(f"[sweep] {key}: {wl.name}", file=sys.stderr, flush=True)
+        ins, outs, host = _device_inputs(wl, device, wl.layers)
+        samples = []
+        for i in range(args.samples):
+            t_ms, _ = _time_steps(va, wl, ins, outs, 1, 3 if i == 0 else 0, stream)
+            samples.append(t_ms * 1e3 / wl.layers)
+        med, p5, p95 = _trimmed(samples)
+        plan = va.Plan([t[0] if wl.layout == 1 else tuple(t) for t in ins], outs=outs,
+                       scale=wl.scale)
+        psamples = []
+        for i in range(args.samples):
+            psamples.append(_time_plan(plan, 1, 3 if i == 0 else 0, stream) * 1e3 / wl.layers)
+        plan.close()
+        pmed, pp5, pp95 = _trimmed(psamples)
+        refs = [oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale)
+                for arrs in host]
+        tf = wl.flops_per_layer / (med * 1e-6) / 1e12
+        out["workloads"][key] = {
+            "workload": wl.name, "layers": wl.layers,
+            "us_per_layer": {"median": med, "p5": p5, "p95": p95},
+            "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
+            "hbm_gbps": wl.bytes_per_layer / (med * 1e-6) / 1e9,
+            "hbm_frac": wl.bytes_per_layer / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "plan_us_per_layer": {"median": pmed, "p5": pp5, "p95": pp95},
+            "parity": _parity(wl, outs, refs),
+        }
+        del ins, outs, host, refs
+        torch.cuda.empty_cache()
+    out["samples"] = args.samples
+    print(json.dumps(out), flush=True)
+
+
 def _cpu_baseline(wl, host, budget_s):
     """Times the fp64 oracle on this host: one full step (every layer, which
     also gives the parity reference), then more layer calls until the time
@@ -187,6 +294,9 @@ def main():
     if args.copy_calib:
         _copy_calibration(args.copy_calib)
         return
+    if args.sweep:
+        _sweep(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
               "forward shards over images with no communication, so the single-GPU "
@@ -232,6 +342,15 @@ def main():
         "roofline": roof,
         "wall_s_timed": wall,
     }
+
+    # the same step recorded once as a plan (one HIP graph of all layer calls)
+    plan = va.Plan([t[0] if wl.layout == 1 else tuple(t) for t in ins], outs=outs, scale=wl.scale)
+    p_ms = _time_plan(plan, args.steps, args.warmup, stream) / args.steps
+    plan.close()
+    result["plan"] = {"ms_per_step": p_ms, "us_per_layer": p_ms * 1e3 / wl.layers,
+                      "tflops": wl.flops_per_layer * wl.layers / (p_ms * 1e-3) / 1e12,
+                      "timing": "the step's layer calls recorded once into a HIP graph "
+                                "(vitattn_plan_create), one graph launch per step"}
 
     if not args.no_cpu_baseline:
         cpu, refs = _cpu_baseline(wl, host, args.cpu_seconds)

@@ -19,8 +19,10 @@
  * Results are deterministic: the same inputs give the same output bits.
  *
  * C ABI only: plain pointers and sizes.  The library allocates no device
- * memory, keeps no state between calls and may be called from several host
- * threads at once.
+ * memory of its own and may be called from several host threads at once.
+ * vitattn_fwd keeps no state between calls; the only state is held in plan
+ * objects (recorded call sequences, below) that the caller creates and
+ * destroys.
  */
 #ifndef VITATTN_H
 #define VITATTN_H
@@ -52,7 +54,8 @@ enum {
   VITATTN_ERR_MISALIGNED = -6,       /* a pointer is not 16-byte aligned */
   VITATTN_ERR_TOO_LARGE = -7,        /* the problem exceeds the launch limits */
   VITATTN_ERR_LAUNCH = -8,           /* the HIP launch reported an error */
-  VITATTN_ERR_OVERLAP = -9           /* out overlaps an input buffer */
+  VITATTN_ERR_OVERLAP = -9,          /* out overlaps an input buffer */
+  VITATTN_ERR_GRAPH = -10            /* recording or launching a HIP graph failed */
 };
 
 /*
@@ -85,6 +88,62 @@ enum {
  */
 int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, void* out, int B, int H,
                 int N, int D, float scale, int layout, void* stream);
+
+/*
+ * Plans: a fixed sequence of forward calls recorded once into a HIP graph and
+ * launched as one unit.  A vision encoder runs the same attention shape once
+ * per layer on buffers that stay in place, so per-call launch work can be
+ * paid once: the FluxVLA "Inference acceleration" tutorial (section 2,
+ * CUDA Graph capture; section 3, preallocated outputs that stay valid inside
+ * a graph) and Realtime-VLA (section 1.2.1) run whole model stages as one
+ * captured graph for this reason.
+ */
+typedef struct vitattn_plan_s* vitattn_plan;
+
+/*
+ * vitattn_plan_create -- records `layers` calls of vitattn_fwd, call l with
+ * the buffers qkv_or_q[l], k[l], v[l], out[l] and the shared sizes, scale and
+ * layout, into one executable HIP graph.  Nothing is computed.
+ *
+ *   plan      receives the new plan, or NULL on error.
+ *   layers    number of recorded calls, >= 1.
+ *   qkv_or_q, out
+ *             host arrays of `layers` device pointers, as for vitattn_fwd.
+ *   k, v      host arrays of `layers` device pointers for the separate
+ *             layout; must be NULL (the arrays themselves) for the packed
+ *             layout.
+ *   B, H, N, D, scale, layout
+ *             as for vitattn_fwd, the same for every call.
+ *
+ * Every call is checked as vitattn_fwd checks it before anything is
+ * recorded; the first failing check's code is returned.  Recording uses a
+ * private stream of default priority on the current device, which the plan
+ * is then bound to.  VITATTN_ERR_GRAPH: the HIP runtime refused to record or
+ * instantiate the graph (or host memory ran out).
+ *
+ * Ownership: the caller owns the plan and every buffer it names; the buffers
+ * must stay allocated, at the same addresses, for as long as the plan is
+ * launched (their contents may change between launches: each launch reads
+ * the inputs as they are then).
+ */
+int vitattn_plan_create(vitattn_plan* plan, int layers, const void* const* qkv_or_q,
+                        const void* const* k, const void* const* v, void* const* out, int B,
+                        int H, int N, int D, float scale, int layout);
+
+/*
+ * vitattn_plan_launch -- enqueues all recorded calls, in order, on `stream`
+ * (a hipStream_t of the plan's device; NULL = the null stream) and returns
+ * without waiting.  Output is bitwise what the same vitattn_fwd calls give.
+ * Errors: VITATTN_ERR_NULL_POINTER (plan is NULL), VITATTN_ERR_GRAPH (the
+ * runtime rejected the graph launch).
+ */
+int vitattn_plan_launch(vitattn_plan plan, void* stream);
+
+/*
+ * vitattn_plan_destroy -- frees the plan (NULL is allowed and ignored).  Work
+ * already enqueued by vitattn_plan_launch still completes.
+ */
+int vitattn_plan_destroy(vitattn_plan plan);
 
 /* Static description of a status code; never NULL. */
 const char* vitattn_strerror(int status);

@@ -146,3 +146,59 @@ def test_python_wrapper_rejects_cpu_tensors(va):
     x = torch.zeros(1, 4, 3, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         va.fwd(x)
+
+
+# ---- plans (recorded call sequences).  Every case below fails a host-side
+# check, or records only empty problems, so no HIP call is made.
+
+def _plan(va, layers=3, q=None, k=None, v=None, out=None, B=2, H=3, N=197, D=64, scale=0.125,
+          layout=None):
+    step = 2 ** 26
+    if q is None:
+        q = [A + l * step for l in range(layers)]
+    if out is None:
+        out = [OUT + l * step for l in range(layers)]
+    if layout is None:
+        layout = va.LAYOUT_PACKED if k is None else va.LAYOUT_SEPARATE
+    return va.plan_create_raw(q, k, v, out, B, H, N, D, scale, layout)
+
+
+def test_plan_rejects_bad_arguments_before_recording(va):
+    b = va._binding
+    assert _plan(va, layers=0, q=[], out=[])[0] == b.ERR_BAD_SIZE
+    rc, handle = _plan(va, D=80)
+    assert rc == b.ERR_UNSUPPORTED_D and handle is None
+    assert _plan(va, scale=math.nan)[0] == b.ERR_BAD_SCALE
+    assert _plan(va, layout=7)[0] == b.ERR_BAD_LAYOUT
+    # one bad call anywhere in the sequence rejects the whole plan
+    q = [A, A + 2 ** 26, A + 2 * 2 ** 26 + 2]
+    assert _plan(va, q=q)[0] == b.ERR_MISALIGNED
+    out = [OUT, A + 2 ** 26 + 64, OUT + 2 * 2 ** 26]  # call 1 writes into its own input
+    assert _plan(va, out=out)[0] == b.ERR_OVERLAP
+    out = [OUT, 0, OUT + 2 * 2 ** 26]
+    assert _plan(va, out=out)[0] == b.ERR_NULL_POINTER
+    # separate layout needs k and v arrays; packed takes none
+    sep = va.LAYOUT_SEPARATE
+    assert _plan(va, layout=sep)[0] == b.ERR_NULL_POINTER
+    kk = [A + 2 ** 30 + l * 2 ** 26 for l in range(3)]
+    assert _plan(va, k=kk, v=kk, layout=va.LAYOUT_PACKED)[0] == b.ERR_BAD_LAYOUT
+
+
+def test_plan_null_handle_arguments(va):
+    lib = va._binding.lib
+    arr = (ctypes.c_void_p * 1)(A)
+    out = (ctypes.c_void_p * 1)(OUT)
+    assert lib.vitattn_plan_create(None, 1, arr, None, None, out, 1, 1, 8, 64, 0.125,
+                                   va.LAYOUT_PACKED) == va._binding.ERR_NULL_POINTER
+    assert va.plan_launch_raw(None, None) == va._binding.ERR_NULL_POINTER
+    assert va.plan_destroy_raw(None) == va.OK
+
+
+def test_plan_of_empty_problems_records_nothing(va):
+    """A plan whose calls are all empty problems holds no graph: creating,
+    launching and destroying it touch no device (the addresses are fake)."""
+    for bhn in [(0, 3, 7), (2, 0, 7), (2, 3, 0)]:
+        rc, handle = _plan(va, B=bhn[0], H=bhn[1], N=bhn[2])
+        assert rc == va.OK and handle
+        assert va.plan_launch_raw(handle, None) == va.OK
+        assert va.plan_destroy_raw(handle) == va.OK

@@ -27,8 +27,10 @@ ERR_MISALIGNED = -6
 ERR_TOO_LARGE = -7
 ERR_LAUNCH = -8
 ERR_OVERLAP = -9
+ERR_GRAPH = -10
 
-EXPORTED = ("vitattn_fwd", "vitattn_strerror", "vitattn_version")
+EXPORTED = ("vitattn_fwd", "vitattn_plan_create", "vitattn_plan_destroy", "vitattn_plan_launch",
+            "vitattn_strerror", "vitattn_version")
 
 
 class VitAttnError(RuntimeError):
@@ -41,12 +43,21 @@ def _load(path: str = LIBRARY):
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is not built: libvitattn has no fallback; build it with "
-            "__graft_entry__.build() or vit_self_attention_amd.build.build()")
+            "__graft_entry__.build() or python vit_self_attention_amd/build.py")
     lib = ctypes.CDLL(path)
     lib.vitattn_fwd.restype = ctypes.c_int
     lib.vitattn_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    ptrs = ctypes.POINTER(ctypes.c_void_p)
+    lib.vitattn_plan_create.restype = ctypes.c_int
+    lib.vitattn_plan_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ptrs, ptrs, ptrs,
+                                        ptrs, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_int]
+    lib.vitattn_plan_launch.restype = ctypes.c_int
+    lib.vitattn_plan_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.vitattn_plan_destroy.restype = ctypes.c_int
+    lib.vitattn_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.vitattn_strerror.restype = ctypes.c_char_p
     lib.vitattn_strerror.argtypes = [ctypes.c_int]
     lib.vitattn_version.restype = ctypes.c_int
@@ -72,19 +83,9 @@ def fwd_raw(qkv_or_q: int, k: int | None, v: int | None, out: int, B: int, H: in
                            int(N), int(D), float(scale), int(layout), stream or None)
 
 
-def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, stream=None):
-    """O = softmax(scale * Q K^T) V per (image, head), on the GPU.
-
-    Packed layout: `fwd(qkv)` with qkv a bf16 CUDA tensor [B, N, 3, H, D]
-    (the fused qkv projection); returns out [B, N, H, D].
-    Separate layout: `fwd(q, k, v)` with q, k, v bf16 CUDA tensors
-    [B, H, N, D]; returns out [B, H, N, D].
-
-    `scale` defaults to 1/sqrt(D).  `out` may be passed preallocated (same
-    device, bf16, contiguous, output shape).  The kernel is enqueued on
-    `stream` (a torch.cuda.Stream; default: the current stream) and the call
-    returns without waiting.
-    """
+def _layout_of(q_or_qkv, k, v, out):
+    """Checks torch tensors as the C ABI expects them; returns
+    (B, H, N, D, layout, out_shape).  `out` may be None."""
     import torch
 
     if (k is None) != (v is None):
@@ -111,12 +112,32 @@ def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, strea
             raise ValueError("q, k, v must have the same shape [B,H,N,D]")
         layout = LAYOUT_SEPARATE
         out_shape = (B, H, N, D)
+    if out is not None:
+        if (not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16
+                or tuple(out.shape) != out_shape or not out.is_contiguous()
+                or out.device != q_or_qkv.device):
+            raise ValueError(f"out must be a contiguous bf16 tensor {out_shape} on the input device")
+    return B, H, N, D, layout, out_shape
+
+
+def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, stream=None):
+    """O = softmax(scale * Q K^T) V per (image, head), on the GPU.
+
+    Packed layout: `fwd(qkv)` with qkv a bf16 CUDA tensor [B, N, 3, H, D]
+    (the fused qkv projection); returns out [B, N, H, D].
+    Separate layout: `fwd(q, k, v)` with q, k, v bf16 CUDA tensors
+    [B, H, N, D]; returns out [B, H, N, D].
+
+    `scale` defaults to 1/sqrt(D).  `out` may be passed preallocated (same
+    device, bf16, contiguous, output shape).  The kernel is enqueued on
+    `stream` (a torch.cuda.Stream; default: the current stream) and the call
+    returns without waiting.
+    """
+    import torch
+
+    B, H, N, D, layout, out_shape = _layout_of(q_or_qkv, k, v, out)
     if out is None:
         out = torch.empty(out_shape, dtype=torch.bfloat16, device=q_or_qkv.device)
-    else:
-        if (out.dtype != torch.bfloat16 or tuple(out.shape) != out_shape
-                or not out.is_contiguous() or out.device != q_or_qkv.device):
-            raise ValueError(f"out must be a contiguous bf16 tensor {out_shape} on the input device")
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     if stream is None:
@@ -127,3 +148,100 @@ def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, strea
     if rc != OK:
         raise VitAttnError(rc, strerror(rc))
     return out
+
+
+def plan_create_raw(qkv_or_q, k, v, out, B: int, H: int, N: int, D: int, scale: float,
+                    layout: int):
+    """Direct call of vitattn_plan_create with lists of raw device addresses
+    (k and v None for the packed layout).  Returns (status, handle)."""
+    layers = len(qkv_or_q)
+    arr = ctypes.c_void_p * max(layers, 1)
+
+    def mk(xs):
+        return None if xs is None else arr(*[x or None for x in xs])
+
+    handle = ctypes.c_void_p()
+    rc = lib.vitattn_plan_create(ctypes.byref(handle), layers, mk(qkv_or_q), mk(k), mk(v), mk(out),
+                                 int(B), int(H), int(N), int(D), float(scale), int(layout))
+    return rc, handle.value
+
+
+def plan_launch_raw(handle, stream: int | None) -> int:
+    return lib.vitattn_plan_launch(handle, stream or None)
+
+
+def plan_destroy_raw(handle) -> int:
+    return lib.vitattn_plan_destroy(handle)
+
+
+class Plan:
+    """A fixed sequence of forward calls recorded once into a HIP graph
+    (vitattn_plan_create) and enqueued as one unit by `launch()`.
+
+        plan = Plan([qkv_0, ..., qkv_L-1], outs=[out_0, ..., out_L-1])
+        plan.launch()            # same results as fwd(qkv_l, out=out_l) for every l
+
+    `inputs` holds one packed qkv tensor per call, or one (q, k, v) tuple per
+    call for the separate layout; every call has the same shape.  `outs`
+    defaults to new tensors (the `outs` attribute).  The tensors must stay
+    alive, unmoved, while the plan is used: it holds references to them.
+    """
+
+    def __init__(self, inputs, outs=None, *, scale: float | None = None):
+        import torch
+
+        if not inputs:
+            raise ValueError("a plan needs at least one call")
+        calls = [(x, None, None) if isinstance(x, torch.Tensor) else tuple(x) for x in inputs]
+        shape = None
+        for (q, k, v) in calls:
+            s = _layout_of(q, k, v, None)
+            if shape is not None and s != shape:
+                raise ValueError("every call of a plan must have the same shape and layout")
+            shape = s
+        B, H, N, D, layout, out_shape = shape
+        if outs is None:
+            outs = [torch.empty(out_shape, dtype=torch.bfloat16, device=calls[0][0].device)
+                    for _ in calls]
+        if len(outs) != len(calls):
+            raise ValueError("one output per call")
+        for (q, k, v), o in zip(calls, outs):
+            _layout_of(q, k, v, o)
+        if scale is None:
+            scale = 1.0 / float(D) ** 0.5
+        self.device = calls[0][0].device
+        self.inputs, self.outs = calls, list(outs)
+        sep = layout == LAYOUT_SEPARATE
+        with torch.cuda.device(self.device):
+            rc, self._handle = plan_create_raw(
+                [c[0].data_ptr() for c in calls], [c[1].data_ptr() for c in calls] if sep else None,
+                [c[2].data_ptr() for c in calls] if sep else None, [o.data_ptr() for o in self.outs],
+                B, H, N, D, scale, layout)
+        if rc != OK:
+            self._handle = None
+            raise VitAttnError(rc, strerror(rc))
+
+    def launch(self, stream=None):
+        """Enqueues every recorded call on `stream` (default: the current
+        stream of the plan's device); returns without waiting."""
+        import torch
+
+        if self._handle is None:
+            raise ValueError("the plan is closed")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        rc = plan_launch_raw(self._handle, stream.cuda_stream)
+        if rc != OK:
+            raise VitAttnError(rc, strerror(rc))
+        return self.outs
+
+    def close(self):
+        if self._handle is not None:
+            plan_destroy_raw(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,6 +1,7 @@
 """Builds libvitattn.so in-tree with hipcc for gfx950.
 
-    python -m vit_self_attention_amd.build
+    python vit_self_attention_amd/build.py      (run as a script: importing the package
+                                                needs the library it builds)
 """
 from __future__ import annotations
 

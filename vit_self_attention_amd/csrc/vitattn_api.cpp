@@ -1,10 +1,15 @@
 // C-ABI entry points of libvitattn: argument validation on the host, then
-// one kernel launch.  Every check here runs before any HIP call, so a bad
-// argument never reaches the device.
+// one kernel launch (vitattn_fwd) or a HIP graph of such launches (plans).
+// Every check runs before any HIP call, so a bad argument never reaches the
+// device.
 #include "vitattn.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <new>
+#include <vector>
 
 #include "vitattn_internal.h"
 
@@ -20,10 +25,12 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   return a0 < b0 + static_cast<uintptr_t>(b_bytes) && b0 < a0 + static_cast<uintptr_t>(a_bytes);
 }
 
-}  // namespace
-
-extern "C" int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, void* out,
-                           int B, int H, int N, int D, float scale, int layout, void* stream) {
+// Checks the arguments of one forward call and fills `a`.  Returns
+// VITATTN_OK with *empty set for a problem with nothing to compute, or a
+// negative code; makes no HIP call.
+int prepare(const void* qkv_or_q, const void* k, const void* v, void* out, int B, int H, int N,
+            int D, float scale, int layout, vitattn::FwdArgs* a, bool* empty) {
+  *empty = false;
   if (layout != VITATTN_LAYOUT_SEPARATE_BHND && layout != VITATTN_LAYOUT_PACKED_BN3HD)
     return VITATTN_ERR_BAD_LAYOUT;
   if (layout == VITATTN_LAYOUT_PACKED_BN3HD && (k != nullptr || v != nullptr))
@@ -33,7 +40,10 @@ extern "C" int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, v
   if (!isfinite(scale)) return VITATTN_ERR_BAD_SCALE;
   // An empty problem has nothing to read or write; its buffers may be NULL
   // (a zero-element tensor usually has no storage).
-  if (B == 0 || H == 0 || N == 0) return VITATTN_OK;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return VITATTN_OK;
+  }
   if (!qkv_or_q || !out) return VITATTN_ERR_NULL_POINTER;
   if (layout == VITATTN_LAYOUT_SEPARATE_BHND && (!k || !v)) return VITATTN_ERR_NULL_POINTER;
   if (!aligned16(qkv_or_q) || !aligned16(out)) return VITATTN_ERR_MISALIGNED;
@@ -61,36 +71,128 @@ extern "C" int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, v
       return VITATTN_ERR_OVERLAP;
   }
 
-  vitattn::FwdArgs a{};
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  a.D = D;
-  a.scale = scale;
-  a.o = static_cast<uint16_t*>(out);
+  *a = vitattn::FwdArgs{};
+  a->B = B;
+  a->H = H;
+  a->N = N;
+  a->D = D;
+  a->scale = scale;
+  a->o = static_cast<uint16_t*>(out);
   const int64_t hd = static_cast<int64_t>(H) * D;
   if (layout == VITATTN_LAYOUT_PACKED_BN3HD) {
     const uint16_t* base = static_cast<const uint16_t*>(qkv_or_q);
-    a.q = base;
-    a.k = base + hd;
-    a.v = base + 2 * hd;
+    a->q = base;
+    a->k = base + hd;
+    a->v = base + 2 * hd;
     const int64_t st = 3 * hd, sb = static_cast<int64_t>(N) * st;
-    a.q_sb = a.k_sb = a.v_sb = sb;
-    a.q_sh = a.k_sh = a.v_sh = D;
-    a.q_st = a.k_st = a.v_st = st;
-    a.o_sb = static_cast<int64_t>(N) * hd;
-    a.o_sh = D;
-    a.o_st = hd;
+    a->q_sb = a->k_sb = a->v_sb = sb;
+    a->q_sh = a->k_sh = a->v_sh = D;
+    a->q_st = a->k_st = a->v_st = st;
+    a->o_sb = static_cast<int64_t>(N) * hd;
+    a->o_sh = D;
+    a->o_st = hd;
   } else {
-    a.q = static_cast<const uint16_t*>(qkv_or_q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
+    a->q = static_cast<const uint16_t*>(qkv_or_q);
+    a->k = static_cast<const uint16_t*>(k);
+    a->v = static_cast<const uint16_t*>(v);
     const int64_t sh = static_cast<int64_t>(N) * D, sb = static_cast<int64_t>(H) * sh;
-    a.q_sb = a.k_sb = a.v_sb = a.o_sb = sb;
-    a.q_sh = a.k_sh = a.v_sh = a.o_sh = sh;
-    a.q_st = a.k_st = a.v_st = a.o_st = D;
+    a->q_sb = a->k_sb = a->v_sb = a->o_sb = sb;
+    a->q_sh = a->k_sh = a->v_sh = a->o_sh = sh;
+    a->q_st = a->k_st = a->v_st = a->o_st = D;
   }
+  return VITATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, void* out,
+                           int B, int H, int N, int D, float scale, int layout, void* stream) {
+  vitattn::FwdArgs a;
+  bool empty;
+  const int st = prepare(qkv_or_q, k, v, out, B, H, N, D, scale, layout, &a, &empty);
+  if (st != VITATTN_OK || empty) return st;
   return vitattn::launch_fwd(a, stream);
+}
+
+// A recorded sequence of forward calls: one executable HIP graph, bound to
+// the device that was current when it was recorded.
+struct vitattn_plan_s {
+  hipGraphExec_t exec = nullptr;  // NULL when every recorded call was empty
+};
+
+extern "C" int vitattn_plan_create(vitattn_plan* plan, int layers, const void* const* qkv_or_q,
+                                   const void* const* k, const void* const* v, void* const* out,
+                                   int B, int H, int N, int D, float scale, int layout) {
+  if (!plan) return VITATTN_ERR_NULL_POINTER;
+  *plan = nullptr;
+  if (layers < 1) return VITATTN_ERR_BAD_SIZE;
+  if (!qkv_or_q || !out) return VITATTN_ERR_NULL_POINTER;
+  const bool separate = layout == VITATTN_LAYOUT_SEPARATE_BHND;
+  if (separate && (!k || !v)) return VITATTN_ERR_NULL_POINTER;
+  if (!separate && (k || v)) return VITATTN_ERR_BAD_LAYOUT;
+  // every call is checked before anything is recorded
+  std::vector<vitattn::FwdArgs> calls;
+  calls.reserve(layers);
+  for (int l = 0; l < layers; ++l) {
+    vitattn::FwdArgs a;
+    bool empty;
+    const int st = prepare(qkv_or_q[l], separate ? k[l] : nullptr, separate ? v[l] : nullptr, out[l],
+                           B, H, N, D, scale, layout, &a, &empty);
+    if (st != VITATTN_OK) return st;
+    if (!empty) calls.push_back(a);
+  }
+  vitattn_plan_s* p = new (std::nothrow) vitattn_plan_s;
+  if (!p) return VITATTN_ERR_GRAPH;
+  if (calls.empty()) {
+    *plan = p;
+    return VITATTN_OK;
+  }
+  // record the calls on a private stream (default priority), in order
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    delete p;
+    return VITATTN_ERR_GRAPH;
+  }
+  int status = VITATTN_OK;
+  hipGraph_t graph = nullptr;
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed) != hipSuccess) {
+    status = VITATTN_ERR_GRAPH;
+  } else {
+    for (const vitattn::FwdArgs& a : calls) {
+      if (vitattn::launch_fwd(a, s) != VITATTN_OK) {
+        status = VITATTN_ERR_GRAPH;
+        break;
+      }
+    }
+    // the capture is always ended, also after a failed launch
+    if (hipStreamEndCapture(s, &graph) != hipSuccess || !graph) status = VITATTN_ERR_GRAPH;
+  }
+  if (status == VITATTN_OK && hipGraphInstantiate(&p->exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    p->exec = nullptr;
+    status = VITATTN_ERR_GRAPH;
+  }
+  if (graph) (void)hipGraphDestroy(graph);
+  (void)hipStreamDestroy(s);
+  if (status != VITATTN_OK) {
+    delete p;
+    return status;
+  }
+  *plan = p;
+  return VITATTN_OK;
+}
+
+extern "C" int vitattn_plan_launch(vitattn_plan plan, void* stream) {
+  if (!plan) return VITATTN_ERR_NULL_POINTER;
+  if (!plan->exec) return VITATTN_OK;
+  return hipGraphLaunch(plan->exec, static_cast<hipStream_t>(stream)) == hipSuccess ? VITATTN_OK
+                                                                                  : VITATTN_ERR_GRAPH;
+}
+
+extern "C" int vitattn_plan_destroy(vitattn_plan plan) {
+  if (!plan) return VITATTN_OK;
+  const bool ok = !plan->exec || hipGraphExecDestroy(plan->exec) == hipSuccess;
+  delete plan;
+  return ok ? VITATTN_OK : VITATTN_ERR_GRAPH;
 }
 
 extern "C" const char* vitattn_strerror(int status) {
@@ -106,6 +208,7 @@ extern "C" const char* vitattn_strerror(int status) {
     case VITATTN_ERR_TOO_LARGE: return "problem exceeds the launch limits";
     case VITATTN_ERR_LAUNCH: return "kernel launch failed";
     case VITATTN_ERR_OVERLAP: return "out overlaps an input buffer";
+    case VITATTN_ERR_GRAPH: return "recording or launching the HIP graph failed";
     default: return "unknown status";
   }
 }
