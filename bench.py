@@ -248,6 +248,45 @@ def _sweep(args):
     print(json.dumps(out), flush=True)
 
 
+def _mfma_probe(stream):
+    """bf16 MFMA throughput of a loop of nothing but 32x32x16 MFMAs
+    (libvitattn_probe), with all-1.0 and with random operands: the measured
+    ceiling next to the vendor peak."""
+    import ctypes
+    import torch
+
+    path = os.path.join(ROOT, "vit_self_attention_amd", "libvitattn_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.vitattn_probe_mfma_loop.restype = ctypes.c_int
+    lib.vitattn_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p]
+    lib.vitattn_probe_mfma_loop_flops.restype = ctypes.c_double
+    lib.vitattn_probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 8 * cus, 1024  # 8 four-wave workgroups (32 waves) per compute unit
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    flops = lib.vitattn_probe_mfma_loop_flops(blocks, iters)
+    res = {}
+    warm, timed = 5, 20  # long enough (about 15 ms) for the clocks to settle under load
+    for name, rnd in (("constant_operands", 0), ("random_operands", 1)):
+        for _ in range(warm):
+            rc = lib.vitattn_probe_mfma_loop(out.data_ptr(), blocks, iters, rnd, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"vitattn_probe_mfma_loop failed: {rc}")
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(timed):
+            lib.vitattn_probe_mfma_loop(out.data_ptr(), blocks, iters, rnd, stream.cuda_stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        res[f"{name}_tflops"] = flops * timed / (t0.elapsed_time(t1) * 1e-3) / 1e12
+    res["kernel"] = ("v_mfma_f32_32x32x16_bf16 only, 4 independent chains per wave, "
+                     f"{blocks} workgroups of 4 waves, {iters} iterations per launch; "
+                     f"{timed} back-to-back launches timed after {warm}")
+    return res
+
+
 def _cpu_baseline(wl, host, budget_s):
     """Times the fp64 oracle on this host: one full step (every layer, which
     also gives the parity reference), then more layer calls until the time
@@ -359,6 +398,10 @@ def main():
     else:
         result["cpu_baseline"] = None
 
+    probe = None if args.no_target else _mfma_probe(stream)
+    if probe is not None:
+        result["mfma_probe"] = probe
+
     if not args.no_target and wl.key != "c5":
         t = WORKLOADS["c5"]
         tins, touts, _ = _device_inputs(t, device, 1)
@@ -376,6 +419,7 @@ def main():
             "hbm_gbps": t.bytes_per_layer / (us * 1e-6) / 1e9,
             "roofline": _roofline(t, us * 1e-6),
             "batches_us_per_layer": batches,
+            "frac_of_measured_random_operand_mfma": tf / probe["random_operands_tflops"],
             "timing": "median of 3 batches of 30 back-to-back launches, each between two HIP "
                       "events on the launch stream, after 30 warmup launches"}
         del tins, touts

@@ -202,3 +202,38 @@ def test_plan_of_empty_problems_records_nothing(va):
         assert rc == va.OK and handle
         assert va.plan_launch_raw(handle, None) == va.OK
         assert va.plan_destroy_raw(handle) == va.OK
+
+
+# ---- the benchmark's MFMA throughput probe (include/vitattn_probe.h)
+
+PROBE_HEADER = os.path.join(ROOT, "include", "vitattn_probe.h")
+
+
+def _probe_lib():
+    from vit_self_attention_amd import build
+    lib = ctypes.CDLL(build.PROBE_LIBRARY)
+    lib.vitattn_probe_mfma_loop.restype = ctypes.c_int
+    lib.vitattn_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p]
+    lib.vitattn_probe_mfma_loop_flops.restype = ctypes.c_double
+    lib.vitattn_probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+def test_probe_library_exports_every_declared_function():
+    with open(PROBE_HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(vitattn_probe_[a-z_]+)\s*\(", text)))
+    assert declared == ["vitattn_probe_mfma_loop", "vitattn_probe_mfma_loop_flops"]
+    lib = _probe_lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_probe_argument_checks_and_flop_count():
+    lib = _probe_lib()
+    assert lib.vitattn_probe_mfma_loop(None, 8, 8, 1, None) == -1
+    assert lib.vitattn_probe_mfma_loop(OUT, 0, 8, 1, None) == -2
+    assert lib.vitattn_probe_mfma_loop(OUT, 8, 0, 1, None) == -2
+    # 4 waves x 4 chains x iters MFMAs of 2*32*32*16 flops per block
+    assert lib.vitattn_probe_mfma_loop_flops(3, 5) == 3 * 4 * 5 * 4 * 2 * 32 * 32 * 16

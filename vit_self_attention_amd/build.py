@@ -33,9 +33,15 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIBRARY + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
+# measurement helper of the benchmark (bf16 MFMA throughput probe), built as
+# a library of its own: not part of the attention path
+PROBE_LIBRARY = os.path.join(PKG, "libvitattn_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "vitattn_probe.hip")]
+
+
+def _hipcc(sources, library, verbose):
+    tmp = library + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *sources]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     text = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line)
@@ -43,7 +49,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{text}")
     if verbose and text.strip():
         print(text, file=sys.stderr)
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, library)
+    return library
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(SOURCES, LIBRARY, verbose)
+    _hipcc(PROBE_SOURCES, PROBE_LIBRARY, verbose)
     return LIBRARY
 
 
