@@ -52,6 +52,8 @@ def _parse():
                    help="skip the 384 px SigLIP (B=48, N=729) figures")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU time budget for the oracle baseline")
+    p.add_argument("--fmt", choices=["bf16", "f16"], default="bf16",
+                   help="element format of inputs and output (f16: the fp16 variant)")
     p.add_argument("--sweep", action="store_true",
                    help="per-workload statistics for all workloads (one JSON line)")
     p.add_argument("--samples", type=int, default=50, help="samples per workload in --sweep")
@@ -76,6 +78,14 @@ def _copy_calibration(mib):
                       "bytes_written_per_copy": n * 4}), flush=True)
 
 
+FMT = "bf16"  # element format of the timed inputs: "bf16" or, with --fmt f16, "f16"
+
+
+def _torch_dtype():
+    import torch
+    return torch.float16 if FMT == "f16" else torch.bfloat16
+
+
 def _device_inputs(wl, device, layers):
     import numpy as np
     import torch
@@ -83,14 +93,14 @@ def _device_inputs(wl, device, layers):
 
     ins, outs, host = [], [], []
     for layer in range(layers):
-        li = make_layer(wl, layer)
+        li = make_layer(wl, layer, fmt=FMT)
         arrs = li.in_layout(wl.layout)
-        ts = [torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+        ts = [torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(_torch_dtype()).to(device)
               if a is not None else None for a in arrs]
         ins.append(ts)
         B, N, H, D = wl.B, wl.N, wl.H, wl.D
         shape = (B, N, H, D) if wl.layout == 1 else (B, H, N, D)
-        outs.append(torch.empty(shape, dtype=torch.bfloat16, device=device))
+        outs.append(torch.empty(shape, dtype=_torch_dtype(), device=device))
         host.append(arrs)
     return ins, outs, host
 
@@ -230,7 +240,7 @@ def _sweep(args):
             psamples.append(_time_plan(plan, 1, 3 if i == 0 else 0, stream) * 1e3 / wl.layers)
         plan.close()
         pmed, pp5, pp95 = _trimmed(psamples)
-        refs = [oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale)
+        refs = [oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale, fmt=FMT)
                 for arrs in host]
         tf = wl.flops_per_layer / (med * 1e-6) / 1e12
         out["workloads"][key] = {
@@ -298,11 +308,11 @@ def _cpu_baseline(wl, host, budget_s):
     refs = []
     t0 = time.perf_counter()
     for arrs in host:
-        refs.append(oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale))
+        refs.append(oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale, fmt=FMT))
     done = len(host)
     while time.perf_counter() - t0 < budget_s:
         arrs = host[done % len(host)]
-        oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale)
+        oracle.attention(*arrs, wl.layout, wl.B, wl.H, wl.N, wl.D, wl.scale, fmt=FMT)
         done += 1
     dt = time.perf_counter() - t0
     tflops = wl.flops_per_layer * done / dt / 1e12
@@ -324,12 +334,16 @@ def _parity(wl, outs_dev, refs):
         tot += float(err.sum())
         cnt += err.size
     mean = tot / cnt
-    return {"max_abs": mx, "mean_abs": mean, "pass": bool(mx <= 2e-2 and mean <= 2e-3),
+    # bf16: the stated bar; fp16: half of it (11 significant bits against 8)
+    tol_max, tol_mean = (1e-2, 1e-3) if FMT == "f16" else (2e-2, 2e-3)
+    return {"max_abs": mx, "mean_abs": mean, "pass": bool(mx <= tol_max and mean <= tol_mean),
             "layers": len(refs)}
 
 
 def main():
+    global FMT
     args = _parse()
+    FMT = args.fmt
     if args.copy_calib:
         _copy_calibration(args.copy_calib)
         return
@@ -370,7 +384,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": FMT,
         "data": "synthetic (seeded numpy PCG64, bf16 RNE)",
         "config": {"workload": wl.name, "B": wl.B, "N": wl.N, "H": wl.H, "D": wl.D,
                    "layout": "packed [B,N,3,H,D]" if wl.layout == 1 else "separate [B,H,N,D]",

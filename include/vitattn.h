@@ -14,8 +14,10 @@
  * qkv projection, with inputs and outputs unchanged.  Every token attends to
  * every token (no mask); no dropout (inference).
  *
- * Numerics: bf16 inputs, fp32 accumulation and softmax state, probabilities
- * rounded to bf16 for the P V product, bf16 output rounded to nearest even.
+ * Numerics: bf16 inputs (or fp16 with VITATTN_DTYPE_FP16), fp32 accumulation
+ * and softmax state, probabilities rounded to the input format (nearest
+ * even) for the P V product, output in the input format rounded to nearest
+ * even.
  * Results are deterministic: the same inputs give the same output bits.
  *
  * C ABI only: plain pointers and sizes.  The library allocates no device
@@ -40,7 +42,13 @@ enum {
    * 1 = K, 2 = V), i.e. the [B, N, 3*H*D] output of the qkv projection;
    * k and v must be NULL.  out: [B][N][H][D], i.e. [B, N, H*D], the input
    * of the output projection. */
-  VITATTN_LAYOUT_PACKED_BN3HD = 1
+  VITATTN_LAYOUT_PACKED_BN3HD = 1,
+  /* Element format flag, OR-ed into `layout`: the inputs and the output are
+   * IEEE fp16 instead of bf16, with the same shapes and strides.  The fp16
+   * autocast of the Pi0 latency report (section 3.2) and the fp16 vision
+   * encoder of the VLA speed-up article (section 3.2) run the encoder in
+   * this format. */
+  VITATTN_DTYPE_FP16 = 16
 };
 
 /* Status codes (0 = success; negative = error, nothing launched). */
@@ -61,11 +69,12 @@ enum {
 /*
  * vitattn_fwd -- O = softmax(scale * Q K^T) V for all B*H (image, head) pairs.
  *
- *   qkv_or_q  device pointer, bf16.  Separate layout: Q [B][H][N][D].
+ *   qkv_or_q  device pointer, bf16 (fp16 with VITATTN_DTYPE_FP16).  Separate
+ *             layout: Q [B][H][N][D].
  *             Packed layout: the fused qkv buffer [B][N][3][H][D].
- *   k, v      device pointers, bf16 [B][H][N][D] for the separate layout;
+ *   k, v      device pointers, [B][H][N][D] for the separate layout;
  *             must be NULL for the packed layout.
- *   out       device pointer, bf16, written in full: [B][H][N][D] (separate)
+ *   out       device pointer, same format, written in full: [B][H][N][D] (separate)
  *             or [B][N][H][D] (packed).  Must not overlap any input.
  *   B, H, N   images, heads, tokens.  Any N >= 1 (not only tile multiples);
  *             B, H or N equal to 0 is an empty problem: returns VITATTN_OK
@@ -73,7 +82,8 @@ enum {
  *   D         head dimension: 64 or 72.
  *   scale     logit scale, any finite value (usually 1/sqrt(D)); 0 gives
  *             uniform attention.
- *   layout    VITATTN_LAYOUT_SEPARATE_BHND or VITATTN_LAYOUT_PACKED_BN3HD.
+ *   layout    VITATTN_LAYOUT_SEPARATE_BHND or VITATTN_LAYOUT_PACKED_BN3HD,
+ *             optionally OR-ed with VITATTN_DTYPE_FP16.
  *   stream    a hipStream_t (NULL = the null stream).  The call only
  *             enqueues one kernel on it and returns without waiting.
  *

@@ -25,6 +25,7 @@ LIBRARY = os.path.join(_HERE, "liboracle.so")
 
 LAYOUT_SEPARATE = 0
 LAYOUT_PACKED = 1
+FORMATS = {"bf16": 0, "f16": 1}  # element formats of the 16-bit inputs
 
 _lib = None
 
@@ -43,6 +44,17 @@ def _bind(lib):
     u16p = ctypes.POINTER(ctypes.c_uint16)
     dp = ctypes.POINTER(ctypes.c_double)
     i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_attention_fmt.restype = ctypes.c_int
+    lib.oracle_attention_fmt.argtypes = [u16p, u16p, u16p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_double, dp, dp]
+    lib.oracle_attention_rows_fmt.restype = ctypes.c_int
+    lib.oracle_attention_rows_fmt.argtypes = [u16p, u16p, u16p, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64,
+                                              dp]
+    lib.oracle_widen.restype = ctypes.c_double
+    lib.oracle_widen.argtypes = [ctypes.c_uint, ctypes.c_int]
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_attention.argtypes = [u16p, u16p, u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp]
@@ -88,11 +100,23 @@ def _check_shapes(qkv_or_q, k, v, layout, B, H, N, D):
         raise ValueError(f"unknown layout {layout}")
 
 
+def _fmt(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown element format {fmt!r}")
+    return FORMATS[fmt]
+
+
+def widen(bits: int, fmt: str = "bf16", lib=None) -> float:
+    """The exact value of one 16-bit pattern in element format `fmt`."""
+    return (lib or load()).oracle_widen(int(bits), _fmt(fmt))
+
+
 def attention(qkv_or_q, k, v, layout: int, B: int, H: int, N: int, D: int, scale: float,
-              want_probs: bool = False, lib=None):
+              want_probs: bool = False, lib=None, fmt: str = "bf16"):
     """O = softmax(scale Q K^T) V for every (image, head), in fp64.
 
-    Inputs are bf16 bit patterns (uint16) in `layout`.  Returns O as float64
+    Inputs are 16-bit patterns (uint16) in `layout`, bf16 or, with
+    fmt="f16", IEEE fp16.  Returns O as float64
     [B, N, H, D] (logical order, whatever the input layout), and P as float64
     [B, H, N, N] too when `want_probs`.
     """
@@ -103,17 +127,17 @@ def attention(qkv_or_q, k, v, layout: int, B: int, H: int, N: int, D: int, scale
     vv, vp = _u16(v)
     out = np.zeros((B, N, H, D), dtype=np.float64)
     probs = np.zeros((B, H, N, N), dtype=np.float64) if want_probs else None
-    rc = lib.oracle_attention(ap, kp, vp, layout, B, H, N, D, float(scale),
-                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                              probs.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
-                              if want_probs else None)
+    rc = lib.oracle_attention_fmt(ap, kp, vp, layout, _fmt(fmt), B, H, N, D, float(scale),
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                  probs.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+                                  if want_probs else None)
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed with {rc}")
     return (out, probs) if want_probs else out
 
 
 def attention_rows(qkv_or_q, k, v, layout: int, B: int, H: int, N: int, D: int, scale: float,
-                   rows, lib=None):
+                   rows, lib=None, fmt: str = "bf16"):
     """O[b, i, h, :] in fp64 for each (b, h, i) triple of `rows` ([R, 3] ints).
 
     Returns float64 [R, D].
@@ -125,9 +149,10 @@ def attention_rows(qkv_or_q, k, v, layout: int, B: int, H: int, N: int, D: int, 
     vv, vp = _u16(v)
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
     out = np.zeros((r.shape[0], D), dtype=np.float64)
-    rc = lib.oracle_attention_rows(ap, kp, vp, layout, B, H, N, D, float(scale),
-                                   r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                   r.shape[0], out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    rc = lib.oracle_attention_rows_fmt(ap, kp, vp, layout, _fmt(fmt), B, H, N, D, float(scale),
+                                       r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                       r.shape[0],
+                                       out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_rows failed with {rc}")
     return out

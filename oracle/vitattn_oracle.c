@@ -11,8 +11,8 @@
  * definition of softmax attention, and this file is that definition written
  * out, with no tiling, fusion or reordering:
  *
- *   for every image b and head h, with Q, K, V the N x D bf16 inputs of
- *   (b, h) widened exactly to double:
+ *   for every image b and head h, with Q, K, V the N x D inputs of (b, h)
+ *   (bf16 or fp16) widened exactly to double:
  *     S[i][j] = scale * sum_d Q[i][d] * K[j][d]
  *     P[i][j] = exp(S[i][j] - max_j' S[i][j']) / sum_j'' exp(S[i][j''] - max_j' S[i][j'])
  *     O[i][d] = sum_j P[i][j] * V[j][d]
@@ -28,7 +28,9 @@
  *                       k and v are ignored
  * Output: double, always in logical order [B][N][H][D].
  *
- * Precision: fp64 throughout; bf16 inputs are widened exactly.
+ * Element formats: bf16 (fmt 0) or IEEE 754 binary16, fp16 (fmt 1); either is
+ * widened exactly to double.
+ * Precision: fp64 throughout.
  * Parallelism: OpenMP over (b, h) pairs, static schedule.
  */
 #include <math.h>
@@ -47,6 +49,22 @@ static double bf16_to_double(uint16_t bits) {
   return (double)f;
 }
 
+/* Exact widening of an IEEE 754 binary16 bit pattern: 1 sign bit, 5
+ * exponent bits (bias 15), 10 fraction bits; exponent 0 holds zero and the
+ * subnormals fraction * 2^-24, exponent 31 infinity and NaN. */
+static double f16_to_double(uint16_t bits) {
+  const int sign = bits >> 15, e = (bits >> 10) & 31, f = bits & 1023;
+  double mag;
+  if (e == 0) mag = ldexp((double)f, -24);
+  else if (e == 31) mag = f ? NAN : INFINITY;
+  else mag = ldexp(1024.0 + f, e - 25);  /* (1 + f/1024) * 2^(e-15) */
+  return sign ? -mag : mag;
+}
+
+static double widen(uint16_t bits, int fmt) {
+  return fmt == 1 ? f16_to_double(bits) : bf16_to_double(bits);
+}
+
 /* Offset, in elements, of element (b, n, h, d) of tensor `which`
  * (0 = Q, 1 = K, 2 = V) in the given layout. */
 static int64_t elem_offset(int layout, int which, int64_t B, int64_t H, int64_t N,
@@ -63,13 +81,13 @@ static const uint16_t* tensor_base(int layout, int which, const uint16_t* qkv_or
 }
 
 /* Gathers the N x D matrix of tensor `which` for (b, h) into dst (row-major). */
-static void gather(double* dst, int layout, int which, const uint16_t* qkv_or_q,
+static void gather(double* dst, int layout, int fmt, int which, const uint16_t* qkv_or_q,
                    const uint16_t* k, const uint16_t* v, int64_t B, int64_t H,
                    int64_t N, int64_t D, int64_t b, int64_t h) {
   const uint16_t* base = tensor_base(layout, which, qkv_or_q, k, v);
   for (int64_t n = 0; n < N; ++n)
     for (int64_t d = 0; d < D; ++d)
-      dst[n * D + d] = bf16_to_double(base[elem_offset(layout, which, B, H, N, D, b, n, h, d)]);
+      dst[n * D + d] = widen(base[elem_offset(layout, which, B, H, N, D, b, n, h, d)], fmt);
 }
 
 /* One query row of one (b, h): q_row[D] is Q_i; fills p_row[N] with P[i][:]
@@ -99,8 +117,9 @@ static void attend_row(const double* q_row, const double* K, const double* V, in
 }
 
 static int check_args(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
-                      int layout, int B, int H, int N, int D) {
+                      int layout, int fmt, int B, int H, int N, int D) {
   if (!qkv_or_q) return -1;
+  if (fmt != 0 && fmt != 1) return -2;
   if (layout != 0 && layout != 1) return -2;
   if (layout == 0 && (!k || !v)) return -1;
   if (B < 0 || H < 0 || N < 0 || D < 1) return -3;
@@ -124,14 +143,15 @@ void oracle_set_threads(int n) {
 }
 
 /*
- * Full forward.  out: [B][N][H][D] doubles.  probs: NULL, or [B][H][N][N]
- * doubles receiving P.  Returns 0, or a negative value on a bad argument
- * (-1 missing pointer, -2 bad layout, -3 bad size, -4 out of memory).
+ * Full forward.  fmt: 0 = bf16 inputs, 1 = fp16.  out: [B][N][H][D] doubles.
+ * probs: NULL, or [B][H][N][N] doubles receiving P.  Returns 0, or a
+ * negative value on a bad argument (-1 missing pointer, -2 bad layout or
+ * format, -3 bad size, -4 out of memory).
  */
-int oracle_attention(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
-                     int layout, int B, int H, int N, int D, double scale, double* out,
-                     double* probs) {
-  int rc = check_args(qkv_or_q, k, v, layout, B, H, N, D);
+int oracle_attention_fmt(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
+                         int layout, int fmt, int B, int H, int N, int D, double scale,
+                         double* out, double* probs) {
+  int rc = check_args(qkv_or_q, k, v, layout, fmt, B, H, N, D);
   if (rc) return rc;
   if (!out) return -1;
   if (B == 0 || H == 0 || N == 0) return 0;
@@ -149,9 +169,9 @@ int oracle_attention(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t
     for (int64_t bh = 0; bh < pairs; ++bh) {
       if (!ok) continue;
       int64_t b = bh / H, h = bh % H;
-      gather(Q, layout, 0, qkv_or_q, k, v, B, H, N, D, b, h);
-      gather(K, layout, 1, qkv_or_q, k, v, B, H, N, D, b, h);
-      gather(V, layout, 2, qkv_or_q, k, v, B, H, N, D, b, h);
+      gather(Q, layout, fmt, 0, qkv_or_q, k, v, B, H, N, D, b, h);
+      gather(K, layout, fmt, 1, qkv_or_q, k, v, B, H, N, D, b, h);
+      gather(V, layout, fmt, 2, qkv_or_q, k, v, B, H, N, D, b, h);
       for (int64_t i = 0; i < N; ++i) {
         attend_row(Q + i * D, K, V, N, D, scale, p, o);
         for (int64_t d = 0; d < D; ++d) out[((b * N + i) * H + h) * D + d] = o[d];
@@ -168,16 +188,23 @@ int oracle_attention(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t
   return failed ? -4 : 0;
 }
 
+/* The full forward on bf16 inputs. */
+int oracle_attention(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
+                     int layout, int B, int H, int N, int D, double scale, double* out,
+                     double* probs) {
+  return oracle_attention_fmt(qkv_or_q, k, v, layout, 0, B, H, N, D, scale, out, probs);
+}
+
 /*
  * Selected rows only, for spot checks of large inputs.  rows: R triples
  * (b, h, i) as int64; out: [R][D] doubles with O[b][i][h][:].  Uses the same
- * per-row routine as oracle_attention().  Returns 0 or a negative error
+ * per-row routine as oracle_attention_fmt().  Returns 0 or a negative error
  * (-5: a triple out of range).
  */
-int oracle_attention_rows(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
-                          int layout, int B, int H, int N, int D, double scale,
-                          const int64_t* rows, int64_t R, double* out) {
-  int rc = check_args(qkv_or_q, k, v, layout, B, H, N, D);
+int oracle_attention_rows_fmt(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
+                              int layout, int fmt, int B, int H, int N, int D, double scale,
+                              const int64_t* rows, int64_t R, double* out) {
+  int rc = check_args(qkv_or_q, k, v, layout, fmt, B, H, N, D);
   if (rc) return rc;
   if (R > 0 && (!rows || !out)) return -1;
   for (int64_t r = 0; r < R; ++r) {
@@ -199,9 +226,9 @@ int oracle_attention_rows(const uint16_t* qkv_or_q, const uint16_t* k, const uin
       int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
       const uint16_t* qb = tensor_base(layout, 0, qkv_or_q, k, v);
       for (int64_t d = 0; d < D; ++d)
-        Q[d] = bf16_to_double(qb[elem_offset(layout, 0, B, H, N, D, b, i, h, d)]);
-      gather(K, layout, 1, qkv_or_q, k, v, B, H, N, D, b, h);
-      gather(V, layout, 2, qkv_or_q, k, v, B, H, N, D, b, h);
+        Q[d] = widen(qb[elem_offset(layout, 0, B, H, N, D, b, i, h, d)], fmt);
+      gather(K, layout, fmt, 1, qkv_or_q, k, v, B, H, N, D, b, h);
+      gather(V, layout, fmt, 2, qkv_or_q, k, v, B, H, N, D, b, h);
       attend_row(Q, K, V, N, D, scale, p, out + r * D);
     }
     if (!ok) {
@@ -212,3 +239,13 @@ int oracle_attention_rows(const uint16_t* qkv_or_q, const uint16_t* k, const uin
   }
   return failed ? -4 : 0;
 }
+
+/* Selected rows on bf16 inputs. */
+int oracle_attention_rows(const uint16_t* qkv_or_q, const uint16_t* k, const uint16_t* v,
+                          int layout, int B, int H, int N, int D, double scale,
+                          const int64_t* rows, int64_t R, double* out) {
+  return oracle_attention_rows_fmt(qkv_or_q, k, v, layout, 0, B, H, N, D, scale, rows, R, out);
+}
+
+/* Exact widening of one 16-bit pattern (fmt 0 bf16, 1 fp16), for tests. */
+double oracle_widen(unsigned bits, int fmt) { return widen((uint16_t)bits, fmt); }

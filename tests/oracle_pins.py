@@ -18,7 +18,7 @@ import numpy as np
 
 import oracle
 from workloads import (LAYOUT_PACKED, LAYOUT_SEPARATE, LayerInputs, bf16_bits_to_f32,
-                       f32_to_bf16_bits)
+                       f16_bits_to_f32, f32_to_bf16_bits, f32_to_f16_bits)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -35,12 +35,21 @@ def _rand_bits(rng, shape, std=1.0):
     return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
 
 
-def _run(lib, q, k, v, scale, layout=LAYOUT_PACKED, want_probs=False):
+def _run(lib, q, k, v, scale, layout=LAYOUT_PACKED, want_probs=False, fmt="bf16"):
     """q, k, v: uint16 [B, N, H, D].  Returns the oracle's O (and P)."""
     B, N, H, D = q.shape
     li = LayerInputs(q, k, v)
     a, kk, vv = li.in_layout(layout)
-    return oracle.attention(a, kk, vv, layout, B, H, N, D, scale, want_probs=want_probs, lib=lib)
+    return oracle.attention(a, kk, vv, layout, B, H, N, D, scale, want_probs=want_probs, lib=lib,
+                            fmt=fmt)
+
+
+def _bits16(x):
+    """float array that is exact in fp16 -> uint16 bits (asserts exactness)."""
+    x = np.asarray(x, dtype=np.float32)
+    b = f32_to_f16_bits(x)
+    assert np.array_equal(f16_bits_to_f32(b), x), "test input not exact in fp16"
+    return b
 
 
 def _f(bits):
@@ -307,6 +316,72 @@ def pin_rows_entry_matches_closed_forms(lib):
     mean_v = _f(vb).mean(axis=1)
     for r, (b, h, i) in enumerate(rows):
         np.testing.assert_allclose(o[r], mean_v[b, h], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- fp16 inputs
+
+def pin_widening_of_every_pattern(lib):
+    """Every one of the 65536 patterns widens to the value numpy's own
+    float16 (IEEE binary16) and bfloat16-as-top-half-of-float32 conversions
+    give (NaN patterns to NaN)."""
+    bits = np.arange(65536, dtype=np.uint16)
+    for fmt, ref in (("f16", bits.view(np.float16).astype(np.float64)),
+                     ("bf16", (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64))):
+        got = np.array([oracle.widen(int(b), fmt, lib=lib) for b in bits])
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), fmt
+        assert np.array_equal(got[~nan], ref[~nan]), fmt
+
+
+def pin_four_token_closed_form_fp16(lib):
+    """The worked 4-token case with fp16 inputs (all its values are exact in
+    fp16) gives the same closed-form outputs."""
+    with open(os.path.join(GOLDEN, "four_token_case.json")) as f:
+        case = json.load(f)
+    for layout in (LAYOUT_PACKED, LAYOUT_SEPARATE):
+        q = np.zeros((1, 4, 1, 72), np.float32)
+        k = np.zeros_like(q)
+        v = np.zeros_like(q)
+        q[0, :, 0, 0] = case["q_col0"]
+        k[0, :, 0, 0] = case["k_col0"]
+        v[0, :, 0, 0] = case["v_col0"]
+        v[0, :, 0, 1] = case["v_col1"]
+        o = _run(lib, _bits16(q), _bits16(k), _bits16(v), case["scale"], layout, fmt="f16")
+        np.testing.assert_allclose(o[0, :, 0, 0], case["expected_o_col0"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(o[0, :, 0, 1], case["expected_o_col1"], rtol=0, atol=1e-12)
+        assert np.all(o[0, :, 0, 2:] == 0.0)
+
+
+def pin_formats_agree_on_shared_values(lib):
+    """Values exact in both bf16 and fp16 (8 significant bits, exponents
+    inside fp16's normal range) give bitwise the same output in either
+    format: only the decoding of the bits differs."""
+    rng = np.random.default_rng(31)
+    B, N, H, D = 2, 19, 3, 72
+    for layout in (LAYOUT_PACKED, LAYOUT_SEPARATE):
+        t = [np.ldexp(rng.integers(-255, 256, (B, N, H, D)).astype(np.float32), -6)
+             for _ in range(3)]
+        ob = _run(lib, *(_bits(x) for x in t), 0.09, layout, fmt="bf16")
+        oh = _run(lib, *(_bits16(x) for x in t), 0.09, layout, fmt="f16")
+        assert np.array_equal(ob, oh)
+
+
+def pin_library_sdpa_fp16(lib):
+    """fp16 inputs against torch's scaled_dot_product_attention in float64
+    on the CPU, with values only fp16 represents (11 significant bits)."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(32)
+    for (B, N, H, D, std) in [(2, 7, 3, 64, 1.0), (2, 41, 2, 72, 2.8)]:
+        t = [f32_to_f16_bits(rng.standard_normal((B, N, H, D)).astype(np.float32) * np.float32(s))
+             for s in (std, std, 1.0)]
+        scale = 1 / math.sqrt(D)
+        o = _run(lib, *t, scale, fmt="f16")
+        tq, tk, tv = (torch.from_numpy(f16_bits_to_f32(x).astype(np.float64).transpose(0, 2, 1, 3).copy())
+                      for x in t)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, scale=scale).numpy().transpose(0, 2, 1, 3)
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
 
 
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -29,6 +29,11 @@ MUTANTS = {
     "separate_b_h_swapped": ("((b * H + h) * N + n) * D + d", "((h * B + b) * N + n) * D + d"),
     "output_in_bhnd_order": ("out[((b * N + i) * H + h) * D + d] = o[d];",
                              "out[((b * H + h) * N + i) * D + d] = o[d];"),
+    "f16_exponent_bias_off_by_one": ("ldexp(1024.0 + f, e - 25)", "ldexp(1024.0 + f, e - 24)"),
+    "f16_subnormal_scale_wrong": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    "f16_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "format_flag_ignored": ("return fmt == 1 ? f16_to_double(bits) : bf16_to_double(bits);",
+                            "return bf16_to_double(bits);"),
     "first_key_skipped": ("for (int64_t j = 0; j < N; ++j) {\n    p_row[j] = exp",
                           "p_row[0] = 0.0;\n  for (int64_t j = 1; j < N; ++j) {\n    p_row[j] = exp"),
 }

@@ -15,6 +15,7 @@ LIBRARY = os.path.join(_HERE, "libvitattn.so")
 
 LAYOUT_SEPARATE = 0  # VITATTN_LAYOUT_SEPARATE_BHND: q, k, v [B,H,N,D]; out [B,H,N,D]
 LAYOUT_PACKED = 1    # VITATTN_LAYOUT_PACKED_BN3HD: qkv [B,N,3,H,D]; out [B,N,H,D]
+DTYPE_FP16 = 16      # VITATTN_DTYPE_FP16, OR-ed into the layout: fp16 instead of bf16
 
 # status codes of include/vitattn.h
 OK = 0
@@ -85,15 +86,19 @@ def fwd_raw(qkv_or_q: int, k: int | None, v: int | None, out: int, B: int, H: in
 
 def _layout_of(q_or_qkv, k, v, out):
     """Checks torch tensors as the C ABI expects them; returns
-    (B, H, N, D, layout, out_shape).  `out` may be None."""
+    (B, H, N, D, layout, out_shape), the layout carrying the fp16 flag for
+    float16 tensors.  `out` may be None."""
     import torch
 
     if (k is None) != (v is None):
         raise ValueError("pass both k and v (separate layout) or neither (packed layout)")
     tensors = [q_or_qkv] + ([k, v] if k is not None else [])
+    dtype = getattr(q_or_qkv, "dtype", None)
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("inputs must be bfloat16 or float16 CUDA tensors")
     for t in tensors:
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise TypeError("inputs must be bfloat16 CUDA tensors")
+        if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+            raise TypeError("inputs must be CUDA tensors of one dtype, bfloat16 or float16")
         if not t.is_contiguous():
             raise ValueError("inputs must be contiguous")
         if t.device != q_or_qkv.device:
@@ -112,24 +117,26 @@ def _layout_of(q_or_qkv, k, v, out):
             raise ValueError("q, k, v must have the same shape [B,H,N,D]")
         layout = LAYOUT_SEPARATE
         out_shape = (B, H, N, D)
+    if dtype == torch.float16:
+        layout |= DTYPE_FP16
     if out is not None:
-        if (not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16
+        if (not isinstance(out, torch.Tensor) or out.dtype != dtype
                 or tuple(out.shape) != out_shape or not out.is_contiguous()
                 or out.device != q_or_qkv.device):
-            raise ValueError(f"out must be a contiguous bf16 tensor {out_shape} on the input device")
+            raise ValueError(f"out must be a contiguous {dtype} tensor {out_shape} on the input device")
     return B, H, N, D, layout, out_shape
 
 
 def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, stream=None):
     """O = softmax(scale * Q K^T) V per (image, head), on the GPU.
 
-    Packed layout: `fwd(qkv)` with qkv a bf16 CUDA tensor [B, N, 3, H, D]
-    (the fused qkv projection); returns out [B, N, H, D].
-    Separate layout: `fwd(q, k, v)` with q, k, v bf16 CUDA tensors
-    [B, H, N, D]; returns out [B, H, N, D].
+    Packed layout: `fwd(qkv)` with qkv a bf16 (or fp16) CUDA tensor
+    [B, N, 3, H, D] (the fused qkv projection); returns out [B, N, H, D].
+    Separate layout: `fwd(q, k, v)` with q, k, v CUDA tensors [B, H, N, D];
+    returns out [B, H, N, D].  The output has the inputs' dtype.
 
     `scale` defaults to 1/sqrt(D).  `out` may be passed preallocated (same
-    device, bf16, contiguous, output shape).  The kernel is enqueued on
+    device and dtype, contiguous, output shape).  The kernel is enqueued on
     `stream` (a torch.cuda.Stream; default: the current stream) and the call
     returns without waiting.
     """
@@ -137,7 +144,7 @@ def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, strea
 
     B, H, N, D, layout, out_shape = _layout_of(q_or_qkv, k, v, out)
     if out is None:
-        out = torch.empty(out_shape, dtype=torch.bfloat16, device=q_or_qkv.device)
+        out = torch.empty(out_shape, dtype=q_or_qkv.dtype, device=q_or_qkv.device)
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     if stream is None:
@@ -201,7 +208,7 @@ class Plan:
             shape = s
         B, H, N, D, layout, out_shape = shape
         if outs is None:
-            outs = [torch.empty(out_shape, dtype=torch.bfloat16, device=calls[0][0].device)
+            outs = [torch.empty(out_shape, dtype=calls[0][0].dtype, device=calls[0][0].device)
                     for _ in calls]
         if len(outs) != len(calls):
             raise ValueError("one output per call")
@@ -211,7 +218,7 @@ class Plan:
             scale = 1.0 / float(D) ** 0.5
         self.device = calls[0][0].device
         self.inputs, self.outs = calls, list(outs)
-        sep = layout == LAYOUT_SEPARATE
+        sep = (layout & ~DTYPE_FP16) == LAYOUT_SEPARATE
         with torch.cuda.device(self.device):
             rc, self._handle = plan_create_raw(
                 [c[0].data_ptr() for c in calls], [c[1].data_ptr() for c in calls] if sep else None,

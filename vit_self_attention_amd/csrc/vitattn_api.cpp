@@ -31,6 +31,8 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 int prepare(const void* qkv_or_q, const void* k, const void* v, void* out, int B, int H, int N,
             int D, float scale, int layout, vitattn::FwdArgs* a, bool* empty) {
   *empty = false;
+  const bool f16 = (layout & VITATTN_DTYPE_FP16) != 0;
+  layout &= ~VITATTN_DTYPE_FP16;
   if (layout != VITATTN_LAYOUT_SEPARATE_BHND && layout != VITATTN_LAYOUT_PACKED_BN3HD)
     return VITATTN_ERR_BAD_LAYOUT;
   if (layout == VITATTN_LAYOUT_PACKED_BN3HD && (k != nullptr || v != nullptr))
@@ -77,6 +79,7 @@ int prepare(const void* qkv_or_q, const void* k, const void* v, void* out, int B
   a->N = N;
   a->D = D;
   a->scale = scale;
+  a->f16 = f16;
   a->o = static_cast<uint16_t*>(out);
   const int64_t hd = static_cast<int64_t>(H) * D;
   if (layout == VITATTN_LAYOUT_PACKED_BN3HD) {
@@ -127,7 +130,7 @@ extern "C" int vitattn_plan_create(vitattn_plan* plan, int layers, const void* c
   *plan = nullptr;
   if (layers < 1) return VITATTN_ERR_BAD_SIZE;
   if (!qkv_or_q || !out) return VITATTN_ERR_NULL_POINTER;
-  const bool separate = layout == VITATTN_LAYOUT_SEPARATE_BHND;
+  const bool separate = (layout & ~VITATTN_DTYPE_FP16) == VITATTN_LAYOUT_SEPARATE_BHND;
   if (separate && (!k || !v)) return VITATTN_ERR_NULL_POINTER;
   if (!separate && (k || v)) return VITATTN_ERR_BAD_LAYOUT;
   // every call is checked before anything is recorded

@@ -14,7 +14,8 @@
 //   * keys in tiles of 64, fetched cooperatively with 128-bit direct-to-LDS
 //     loads into a ring of LDS stages (row-major K and V), three tiles ahead
 //     of the tile being reduced, one barrier per tile;
-//   * both products on bf16 MFMA with fp32 accumulation, in transposed form:
+//   * both products on 16-bit MFMA (bf16, or fp16 for fp16 inputs) with fp32
+//     accumulation, in transposed form:
 //       S^T = K Q^T       (v_mfma_f32_32x32x16_bf16; D = 72 adds a 32x32x8)
 //       O^T += V^T P^T    (v_mfma_f32_32x32x16_bf16)
 //     With S^T in the accumulator layout, lane l holds 16 keys of query
@@ -60,10 +61,14 @@ constexpr int kBlockN = 64;           // keys per tile
 constexpr int kKStride = 72;          // K row stride in LDS (elements): 144 B
 constexpr float kLog2e = 1.4426950408889634f;
 // The running max is lazy: it moves (and the accumulator is rescaled) only
-// when a row's max grows by more than 2^kLazy.  Weights then stay below
-// 2^64 and row sums below N * 2^64, far inside fp32 range, while bf16
-// rounding of a weight is relative and so independent of the shift.
-constexpr float kLazy = 64.0f;
+// when a row's max grows by more than 2^lazy.  Weights then stay below
+// 2^lazy and row sums below N * 2^lazy, inside fp32 range, while rounding a
+// weight to 16 bits is relative and so independent of the shift.  bf16 has
+// fp32's exponent range (lazy = 64); fp16 tops out near 2^16, so its weights
+// are kept below 2^8 (and those under 2^-24 of the row max, negligible
+// against it, flush to zero).
+template <bool kF16>
+constexpr float lazy_bound() { return kF16 ? 8.0f : 64.0f; }
 
 struct KernelArgs {
   const uint16_t* q;
@@ -84,12 +89,57 @@ struct KernelArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 p;
-  p[0] = static_cast<__bf16>(lo);
-  p[1] = static_cast<__bf16>(hi);
-  return __builtin_bit_cast(uint32_t, p);
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest-even 16-bit values (bf16 or fp16), packed
+// low/high into 32 bits (one v_cvt_pk_*_f32 on gfx950).
+template <bool kF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (kF16) {
+    f16x2 p;
+    p[0] = static_cast<_Float16>(lo);
+    p[1] = static_cast<_Float16>(hi);
+    return __builtin_bit_cast(uint32_t, p);
+  } else {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 p;
+    p[0] = static_cast<__bf16>(lo);
+    p[1] = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, p);
+  }
+}
+
+// 16-bit input elements travel in bf16-typed vectors whatever their format;
+// the MFMA wrappers reinterpret them for the fp16 instructions.
+template <bool kF16>
+__device__ __forceinline__ f32x16 mma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                  c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool kF16>
+__device__ __forceinline__ f32x16 mma_32x32x8(bf16x4 a, bf16x4 b, f32x16 c) {
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
+}
+// acc + w.lo + w.hi for two packed 16-bit weights (v_dot2 with (1, 1))
+template <bool kF16>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  if constexpr (kF16) {
+    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
+  } else {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  }
 }
 
 // v_permlane32_swap exchanges the upper half of its first operand with the
@@ -167,7 +217,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 // a workgroup share one block of 32 queries, wave w reduces key tile w, and
 // the partial results are merged through LDS at the end.  This gives four
 // times the waves for grids too small to fill the chip.
-template <int D, int NW, bool kSplit>
+template <int D, int NW, bool kSplit, bool kF16>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
   constexpr int kOutTiles = kOnesRow ? 3 : 2;
@@ -265,7 +315,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // V, so no other wave's write needs to be visible to it.
   auto write_ones = [&](int stage) __attribute__((always_inline)) {
     if constexpr (kOnesRow) {
-      const u32x4 w = {0x3f80u, 0u, 0u, 0u};
+      const u32x4 w = {kF16 ? 0x3c00u : 0x3f80u, 0u, 0u, 0u};  // 1.0
       *reinterpret_cast<u32x4*>(&lds[stage * kStageElems + kKTile + lane * kVStride + 72]) = w;
     }
   };
@@ -449,11 +499,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(kt, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+      s[i & 1] = mma_32x32x16<kF16>(k_read(kt, i), qf[i >> 1], s[i & 1]);
     if constexpr (D == 72) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(k_read_tail(kt, blk), qt, s[blk], 0, 0, 0);
+        s[blk] = mma_32x32x8<kF16>(k_read_tail(kt, blk), qt, s[blk]);
     }
   };
   // V^T operand of P V step idx = t*kOutTiles + mt (keys 16t.., output rows 32mt..)
@@ -482,8 +532,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     return max_across_halves(
         fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7]))));
   };
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  constexpr float kLazy = lazy_bound<kF16>();
   float psum = 0.f;  // D = 64: row sum of the bf16 weights (dot products with ones)
   f32x16 acc[kOutTiles];
 #pragma unroll
@@ -545,10 +594,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         if constexpr (kRagged) p[e] = kb + key_of(e) < N ? p[e] : 0.f;
         if (e & 1) {
           const int k = e >> 1;
-          w[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+          w[k] = pack2<kF16>(p[2 * k], p[2 * k + 1]);
           if constexpr (!kOnesRow)
-            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]), ones2, psum,
-                                                   false);
+            psum = add_pair<kF16>(w[k], psum);
         }
       };
       auto pb = [&](int t) {
@@ -576,9 +624,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         for (int i = 0; i < kQk; ++i) {
           if (i + 2 < kQk) fetch_k(i + 2);
           if (i < 8)
-            nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[i], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+            nxt[i & 1] = mma_32x32x16<kF16>(ko[i], qf[i >> 1], nxt[i & 1]);
           else
-            nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ko4[i - 8], qt, nxt[i & 1], 0, 0, 0);
+            nxt[i & 1] = mma_32x32x8<kF16>(ko4[i - 8], qt, nxt[i & 1]);
 #pragma unroll
           for (int e = 24 * i / kQk; e < 24 * (i + 1) / kQk; ++e) do_exp(e);
           __builtin_amdgcn_sched_barrier(0);
@@ -600,7 +648,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       for (int i = 0; i < kPv; ++i) {
         if (i + 2 < kPv) vo[i + 2] = v_read(vt, i + 2);
         const int t = i / kOutTiles, mt = i % kOutTiles;
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[i], pb(t), acc[mt], 0, 0, 0);
+        acc[mt] = mma_32x32x16<kF16>(vo[i], pb(t), acc[mt]);
         if (i < kHalfPv) {
 #pragma unroll
           for (int e = 24 + 8 * i / kHalfPv; e < 24 + 8 * (i + 1) / kHalfPv; ++e) do_exp(e);
@@ -716,8 +764,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) o += sc[w] * *reinterpret_cast<const f32x4*>(slot(w, mt * 4 + wave));
           u32x2 st;
-          st[0] = pack_bf16x2(o[0] * inv, o[1] * inv);
-          st[1] = pack_bf16x2(o[2] * inv, o[3] * inv);
+          st[0] = pack2<kF16>(o[0] * inv, o[1] * inv);
+          st[1] = pack2<kF16>(o[2] * inv, o[3] * inv);
           *reinterpret_cast<u32x2*>(orow + d0) = st;
         }
       }
@@ -796,8 +844,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
             const int d0 = 32 * mt + 8 * g + 4 * half;
             if (d0 < D) {
               u32x2 w;
-              w[0] = pack_bf16x2(acc[mt][4 * g + 0] * inv, acc[mt][4 * g + 1] * inv);
-              w[1] = pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv);
+              w[0] = pack2<kF16>(acc[mt][4 * g + 0] * inv, acc[mt][4 * g + 1] * inv);
+              w[1] = pack2<kF16>(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv);
               *reinterpret_cast<u32x2*>(ob + col * kOS + d0) = w;
             }
           }
@@ -822,9 +870,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   }
 }
 
-template <int D, int NW, bool kSplit>
+template <int D, int NW, bool kSplit, bool kF16>
 int launch(const KernelArgs& ka, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit, kF16>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka);
   return hipGetLastError() == hipSuccess ? VITATTN_OK : VITATTN_ERR_LAUNCH;
 }
 
@@ -861,6 +909,24 @@ int pick_waves(int B, int H, int N) {
   return 1;
 }
 
+namespace {
+
+template <bool kF16>
+int launch_typed(const KernelArgs& ka, int D, int nw, hipStream_t s) {
+  if (D == 64) {
+    if (nw == -4) return launch<64, 4, true, kF16>(ka, s);
+    if (nw == 4) return launch<64, 4, false, kF16>(ka, s);
+    if (nw == 2) return launch<64, 2, false, kF16>(ka, s);
+    return launch<64, 1, false, kF16>(ka, s);
+  }
+  if (nw == -4) return launch<72, 4, true, kF16>(ka, s);
+  if (nw == 4) return launch<72, 4, false, kF16>(ka, s);
+  if (nw == 2) return launch<72, 2, false, kF16>(ka, s);
+  return launch<72, 1, false, kF16>(ka, s);
+}
+
+}  // namespace
+
 int launch_fwd(const FwdArgs& f, void* stream) {
   KernelArgs ka{};
   ka.q = f.q;
@@ -891,16 +957,7 @@ int launch_fwd(const FwdArgs& f, void* stream) {
     if (slots >= 16 && slots % 8 == 0 && ka.items >= 2 * slots) ka.grid = slots;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (f.D == 64) {
-    if (nw == -4) return launch<64, 4, true>(ka, s);
-    if (nw == 4) return launch<64, 4, false>(ka, s);
-    if (nw == 2) return launch<64, 2, false>(ka, s);
-    return launch<64, 1, false>(ka, s);
-  }
-  if (nw == -4) return launch<72, 4, true>(ka, s);
-  if (nw == 4) return launch<72, 4, false>(ka, s);
-  if (nw == 2) return launch<72, 2, false>(ka, s);
-  return launch<72, 1, false>(ka, s);
+  return f.f16 ? launch_typed<true>(ka, f.D, nw, s) : launch_typed<false>(ka, f.D, nw, s);
 }
 
 }  // namespace vitattn

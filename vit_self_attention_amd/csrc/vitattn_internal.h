@@ -6,7 +6,7 @@
 
 namespace vitattn {
 
-// Per-launch description of one attention problem.  Strides are in bf16
+// Per-launch description of one attention problem.  Strides are in 16-bit
 // elements.  For (image b, head h, token n) the row of Q starts at
 // q + b*q_sb + h*q_sh + n*q_st, and likewise for k, v and out.
 struct FwdArgs {
@@ -20,6 +20,7 @@ struct FwdArgs {
   int64_t o_sb, o_sh, o_st;
   int B, H, N, D;
   float scale;
+  bool f16;  // elements are fp16 (true) or bf16 (false): inputs, probabilities, output
 };
 
 // Enqueues the forward kernel on `stream` (a hipStream_t).  Arguments are

@@ -108,6 +108,25 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE fp16 (numpy's conversion: round to
+    nearest, ties to even).  Returns the 16-bit patterns as uint16; inputs
+    must lie inside fp16's range."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.size and float(np.abs(x).max()) >= 65520.0:
+        raise ValueError("value outside the fp16 range")
+    return x.astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of fp16 bit patterns to float32."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+ROUND = {"bf16": f32_to_bf16_bits, "f16": f32_to_f16_bits}
+WIDEN = {"bf16": bf16_bits_to_f32, "f16": f16_bits_to_f32}
+
+
 @dataclass
 class LayerInputs:
     """Bits of one layer's Q, K, V in the logical order [B, N, H, D]."""
@@ -144,18 +163,20 @@ def gamma_vectors(wl: Workload) -> np.ndarray:
 
 
 def make_layer(wl: Workload, layer: int, *, B: int | None = None, N: int | None = None,
-               H: int | None = None) -> LayerInputs:
+               H: int | None = None, fmt: str = "bf16") -> LayerInputs:
     """Draw one layer's inputs for workload `wl`.
 
     `B`, `N`, `H` override the workload's sizes (for reduced-size parity cases
-    with the same value recipe).
+    with the same value recipe).  `fmt` is the 16-bit format the float32
+    draws are rounded to: "bf16" (the workloads' own) or "f16"; the draws are
+    the same for both.
 
     Recipes:
       iid    : Q, K, V i.i.d. N(0, 1).
       gamma  : Q, K, V = z * gamma[h*D + d], z ~ N(0, 1), gamma from gamma_vectors().
       stress : Q, K ~ N(0, 2.8^2) so that logits have std ~8 at scale 1/sqrt(D);
                V ~ N(0, 1). In every (b, h), round(0.1*N) distinct query rows i
-               get one uniformly chosen key j added: Q_i <- bf16(Q_i + K_j),
+               get one uniformly chosen key j added: Q_i <- round(Q_i + K_j),
                which makes that key dominate row i (near one-hot softmax).
     """
     B = wl.B if B is None else B
@@ -179,9 +200,10 @@ def make_layer(wl: Workload, layer: int, *, B: int | None = None, N: int | None 
         k = k * np.float32(2.8)
     else:
         raise ValueError(f"unknown recipe {wl.kind}")
-    qb = f32_to_bf16_bits(q)
-    kb = f32_to_bf16_bits(k)
-    vb = f32_to_bf16_bits(v)
+    rnd, wid = ROUND[fmt], WIDEN[fmt]
+    qb = rnd(q)
+    kb = rnd(k)
+    vb = rnd(v)
     if wl.kind == "stress":
         n_boost = int(round(0.1 * N))
         if n_boost > 0:
@@ -189,9 +211,9 @@ def make_layer(wl: Workload, layer: int, *, B: int | None = None, N: int | None 
             keys = rng.integers(0, N, size=(B, H, n_boost))
             bi = np.arange(B)[:, None, None]
             hi = np.arange(H)[None, :, None]
-            qf = bf16_bits_to_f32(qb)
-            kf = bf16_bits_to_f32(kb)
+            qf = wid(qb)
+            kf = wid(kb)
             boosted = qf[bi, rows, hi, :] + kf[bi, keys, hi, :]
             qf[bi, rows, hi, :] = boosted
-            qb = f32_to_bf16_bits(qf)
+            qb = rnd(qf)
     return LayerInputs(qb, kb, vb)
