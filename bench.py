@@ -297,6 +297,68 @@ def _mfma_probe(stream):
     return res
 
 
+def _linear_figures(stream, steps=20):
+    """The qkv projection and the output projection (bias + residual) of
+    SigLIP-So400m (1152 -> 3456 and 1152 -> 1152) at 224 px x 2 and 384 px
+    x 48, through vitattn_linear: time per call (HIP events over `steps`
+    back-to-back calls after 3), TFLOP/s, roofline, and parity of sampled
+    rows with the fp64 oracle."""
+    import numpy as np
+    import torch
+    import vit_self_attention_amd as va
+    from oracle import linear as lo
+    from workloads import f32_to_bf16_bits
+
+    res = {}
+    rng = np.random.default_rng(7)
+    dev = torch.device("cuda:0")
+    for name, M, Nout, resid in (("qkv_224x2", 2 * 256, 3456, False),
+                                 ("qkv_384x48", 48 * 729, 3456, False),
+                                 ("proj_384x48", 48 * 729, 1152, True)):
+        K = 1152
+        x = f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        w = f32_to_bf16_bits(rng.standard_normal((Nout, K)).astype(np.float32) / np.float32(34.0))
+        b = f32_to_bf16_bits(rng.standard_normal(Nout).astype(np.float32) * np.float32(0.1))
+        r = f32_to_bf16_bits(rng.standard_normal((M, Nout)).astype(np.float32)) if resid else None
+
+        def dv(a):
+            return None if a is None else torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        xd, wd, bd, rd = dv(x), dv(w), dv(b), dv(r)
+        out = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            va.linear(xd, wd, bd, rd, out=out, stream=stream)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            va.linear(xd, wd, bd, rd, out=out, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / steps
+        flops = 2.0 * M * K * Nout
+        tf = flops / (us * 1e-6) / 1e12
+        nbytes = 2.0 * (M * K + Nout * K + M * Nout * (2 if resid else 1) + Nout)
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 30)]))
+        got = lo.widen(out.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+        ref = lo.linear_rows(x, w, b, r, rows)
+        err = np.abs(got - ref)
+        res[name] = {"M": M, "K": K, "Nout": Nout, "bias": True, "residual": resid,
+                     "us_per_call": us, "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
+                     "roofline": {"bound": "mfma" if flops / nbytes >= RIDGE else "hbm",
+                                  "achieved": tf if flops / nbytes >= RIDGE else nbytes / (us * 1e-6) / 1e9,
+                                  "peak": PEAK_BF16_TFLOPS if flops / nbytes >= RIDGE else PEAK_HBM_GBPS,
+                                  "unit": "TFLOP/s" if flops / nbytes >= RIDGE else "GB/s"},
+                     "sampled_rows_max_abs_err": float(err.max()),
+                     "sampled_rows_max_rel_err": float((err / (np.abs(ref) + 1e-3)).max())}
+        r_ = res[name]["roofline"]
+        r_["frac"] = r_["achieved"] / r_["peak"]
+        del xd, wd, bd, rd, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def _cpu_baseline(wl, host, budget_s):
     """Times the fp64 oracle on this host: one full step (every layer, which
     also gives the parity reference), then more layer calls until the time
@@ -411,6 +473,9 @@ def main():
         result["parity"] = _parity(wl, outs, refs)
     else:
         result["cpu_baseline"] = None
+
+    if not args.no_target and FMT == "bf16":
+        result["linear"] = _linear_figures(stream)
 
     probe = None if args.no_target else _mfma_probe(stream)
     if probe is not None:

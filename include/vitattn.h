@@ -63,7 +63,8 @@ enum {
   VITATTN_ERR_TOO_LARGE = -7,        /* the problem exceeds the launch limits */
   VITATTN_ERR_LAUNCH = -8,           /* the HIP launch reported an error */
   VITATTN_ERR_OVERLAP = -9,          /* out overlaps an input buffer */
-  VITATTN_ERR_GRAPH = -10            /* recording or launching a HIP graph failed */
+  VITATTN_ERR_GRAPH = -10,           /* recording or launching a HIP graph failed */
+  VITATTN_ERR_UNSUPPORTED_SHAPE = -11 /* vitattn_linear: K or Nout not supported */
 };
 
 /*
@@ -154,6 +155,45 @@ int vitattn_plan_launch(vitattn_plan plan, void* stream);
  * already enqueued by vitattn_plan_launch still completes.
  */
 int vitattn_plan_destroy(vitattn_plan plan);
+
+/*
+ * vitattn_linear -- the linear layers on either side of the attention in a
+ * ViT block, on the same hardware path (bf16 or fp16 MFMA, fp32 accumulate):
+ *
+ *     out[m][n] = sum_k x[m][k] * w[n][k] + bias[n] + residual[m][n]
+ *
+ * Two uses: the block's fused qkv projection, whose [M][3*H*D] output with
+ * M = B*N is exactly the packed [B][N][3][H][D] buffer vitattn_fwd reads
+ * (the FluxVLA "Inference acceleration" tutorial, section 1, fuses this
+ * projection; the Pi0 Flash Attention tutorial, section 3.2, feeds the
+ * attention from it), and the output projection with its bias and the
+ * block's residual add in one pass (the same FluxVLA tutorial, section 3).
+ *
+ *   x         device pointer, [M][K] row-major (tokens x input features).
+ *   w         device pointer, [Nout][K] row-major: the layer's weight as
+ *             stored (output features x input features).
+ *   bias      device pointer to [Nout], or NULL for no bias.
+ *   residual  device pointer to [M][Nout], or NULL for none.  May be equal
+ *             to `out` (an in-place residual add) but must not overlap it
+ *             otherwise.
+ *   out       device pointer, [M][Nout], written in full; must not overlap
+ *             x, w or bias.
+ *   M, K, Nout  sizes: M >= 0 (any value), K a positive multiple of 32,
+ *             Nout a multiple of 8 (else VITATTN_ERR_UNSUPPORTED_SHAPE);
+ *             M * K and Nout * K below 2^31 elements.  M or Nout equal to
+ *             0 is an empty problem (returns VITATTN_OK, launches nothing).
+ *   flags     0 for bf16 tensors, VITATTN_DTYPE_FP16 for fp16 (all tensors
+ *             in the one format); other bits: VITATTN_ERR_BAD_LAYOUT.
+ *   stream    a hipStream_t (NULL = the null stream); the call enqueues one
+ *             kernel and returns without waiting.
+ *
+ * Numerics: 16-bit inputs, fp32 accumulation of the products, bias and
+ * residual added in fp32, one rounding (nearest even) to the output format.
+ * Deterministic.  Ownership, alignment (16 bytes) and error behaviour as
+ * for vitattn_fwd.
+ */
+int vitattn_linear(const void* x, const void* w, const void* bias, const void* residual,
+                   void* out, int M, int K, int Nout, int flags, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* vitattn_strerror(int status);

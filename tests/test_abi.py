@@ -237,3 +237,38 @@ def test_probe_argument_checks_and_flop_count():
     assert lib.vitattn_probe_mfma_loop(OUT, 8, 0, 1, None) == -2
     # 4 waves x 4 chains x iters MFMAs of 2*32*32*16 flops per block
     assert lib.vitattn_probe_mfma_loop_flops(3, 5) == 3 * 4 * 5 * 4 * 2 * 32 * 32 * 16
+
+
+# ---- vitattn_linear argument checks (all fail before any HIP call)
+
+def _lin(va, x=A, w=A + 2 ** 30, bias=None, residual=None, out=OUT, M=64, K=128, Nout=64, flags=0):
+    return va.linear_raw(x, w, bias, residual, out, M, K, Nout, flags, None)
+
+
+def test_linear_argument_checks(va):
+    b = va._binding
+    assert _lin(va, flags=4) == b.ERR_BAD_LAYOUT
+    assert _lin(va, M=-1) == b.ERR_BAD_SIZE
+    assert _lin(va, K=-32) == b.ERR_BAD_SIZE
+    for K in (0, 16, 100, 1150):
+        assert _lin(va, K=K) == b.ERR_UNSUPPORTED_SHAPE, K
+    for Nout in (4, 12, 1001):
+        assert _lin(va, Nout=Nout) == b.ERR_UNSUPPORTED_SHAPE, Nout
+    assert _lin(va, x=0) == b.ERR_NULL_POINTER
+    assert _lin(va, w=0) == b.ERR_NULL_POINTER
+    assert _lin(va, out=0) == b.ERR_NULL_POINTER
+    assert _lin(va, x=A + 8) == b.ERR_MISALIGNED
+    assert _lin(va, bias=A + 2 ** 31 + 4) == b.ERR_MISALIGNED
+    assert _lin(va, residual=OUT + 2 ** 31 + 2) == b.ERR_MISALIGNED
+    assert _lin(va, M=2 ** 21, K=1024) == b.ERR_TOO_LARGE  # x spans 4 GiB
+    # out overlapping x, w or bias; a residual shifted against out
+    assert _lin(va, out=A + 256) == b.ERR_OVERLAP
+    assert _lin(va, out=A + 2 ** 30 + 64) == b.ERR_OVERLAP
+    assert _lin(va, bias=OUT + 64) == b.ERR_OVERLAP
+    assert _lin(va, residual=OUT + 128) == b.ERR_OVERLAP
+
+
+def test_linear_empty_is_a_noop(va):
+    assert _lin(va, M=0) == va.OK
+    assert _lin(va, Nout=0) == va.OK
+    assert _lin(va, M=0, x=0, out=0) == va.OK

@@ -24,22 +24,31 @@ pytestmark = pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc") and sh
                                 reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+def _compile(tmp_path_factory, source):
     from vit_self_attention_amd import build as b
-    out = tmp_path_factory.mktemp("codegen") / "fwd.s"
+    out = tmp_path_factory.mktemp("codegen") / (source + ".s")
     flags = [f for f in b.FLAGS if f not in ("-shared", "-fPIC")]
     cmd = [b.HIPCC, *flags, "-S", "--cuda-device-only", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", str(out), os.path.join(CSRC, "vitattn_fwd.hip")]
+           "-o", str(out), os.path.join(CSRC, source)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-4000:]
     return out.read_text()
 
 
-def _kernels(text):
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "vitattn_fwd.hip")
+
+
+@pytest.fixture(scope="module")
+def linear_asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "vitattn_linear.hip")
+
+
+def _kernels(text, kind="fwd_kernel"):
     """{kernel symbol: (body instruction lines, metadata tail)}"""
     out = {}
-    for m in re.finditer(r"^(_Z\S*fwd_kernel\S*):[ \t]*(?:;.*)?$", text, re.M):
+    for m in re.finditer(r"^(_Z\S*" + kind + r"\S*):[ \t]*(?:;.*)?$", text, re.M):
         end = text.index(".Lfunc_end", m.end())
         body = [ln.strip() for ln in text[m.end():end].splitlines()]
         body = [ln.split(";")[0].strip() for ln in body if ln and not ln.startswith((";", "."))]
@@ -77,3 +86,17 @@ def test_no_scratch_and_two_waves_per_simd(asm):
         nw = int(re.search(r"fwd_kernelILi\d+ELi(\d+)E", name).group(1))
         if nw == 4:
             assert total <= 256, (name, total)
+
+
+def test_linear_kernels_m0_and_registers(linear_asm):
+    """The linear kernels use the same direct-to-LDS fetch sequence, spill
+    nothing and fit two waves per SIMD."""
+    ks = _kernels(linear_asm, "linear_kernel")
+    assert len(ks) == 4, list(ks)  # two tile shapes x {bf16, fp16}
+    for name, (body, meta) in ks.items():
+        for i, ln in enumerate(body):
+            if "m0" in ln:
+                assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", ln), (name, ln)
+                assert body[i + 1] == "s_nop 0" and body[i + 2].startswith("global_load_lds_dwordx4")
+        assert int(re.search(r"ScratchSize: (\d+)", meta).group(1)) == 0, name
+        assert int(re.search(r"TotalNumVgprs: (\d+)", meta).group(1)) <= 256, name

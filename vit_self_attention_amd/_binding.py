@@ -29,9 +29,10 @@ ERR_TOO_LARGE = -7
 ERR_LAUNCH = -8
 ERR_OVERLAP = -9
 ERR_GRAPH = -10
+ERR_UNSUPPORTED_SHAPE = -11
 
-EXPORTED = ("vitattn_fwd", "vitattn_plan_create", "vitattn_plan_destroy", "vitattn_plan_launch",
-            "vitattn_strerror", "vitattn_version")
+EXPORTED = ("vitattn_fwd", "vitattn_linear", "vitattn_plan_create", "vitattn_plan_destroy",
+            "vitattn_plan_launch", "vitattn_strerror", "vitattn_version")
 
 
 class VitAttnError(RuntimeError):
@@ -59,6 +60,8 @@ def _load(path: str = LIBRARY):
     lib.vitattn_plan_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.vitattn_plan_destroy.restype = ctypes.c_int
     lib.vitattn_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.vitattn_linear.restype = ctypes.c_int
+    lib.vitattn_linear.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
     lib.vitattn_strerror.restype = ctypes.c_char_p
     lib.vitattn_strerror.argtypes = [ctypes.c_int]
     lib.vitattn_version.restype = ctypes.c_int
@@ -252,3 +255,58 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def linear_raw(x: int, w: int, bias: int | None, residual: int | None, out: int, M: int, K: int,
+               Nout: int, flags: int, stream: int | None) -> int:
+    """Direct call of vitattn_linear with raw device addresses; returns the status."""
+    return lib.vitattn_linear(x or None, w or None, bias or None, residual or None, out or None,
+                              int(M), int(K), int(Nout), int(flags), stream or None)
+
+
+def linear(x, w, bias=None, residual=None, *, out=None, stream=None):
+    """out = x @ w.T + bias (+ residual) on the GPU (vitattn_linear).
+
+    x: [..., K] CUDA tensor (bf16 or fp16, contiguous; the leading dimensions
+    are the M tokens), w: [Nout, K] (the layer's weight as stored), bias:
+    [Nout] or None, residual: None or a tensor of the output's shape (it may
+    be `out` itself).  Returns out [..., Nout] in the inputs' dtype.  For the
+    fused qkv projection of a ViT block, out [B, N, 3*H*D] viewed as
+    [B, N, 3, H, D] is the packed input of `fwd`.
+    """
+    import torch
+
+    dtype = getattr(x, "dtype", None)
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("x must be a bfloat16 or float16 CUDA tensor")
+    ts = [t for t in (x, w, bias, residual, out) if t is not None]
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+            raise TypeError("all tensors must be CUDA tensors of x's dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.device != x.device:
+            raise ValueError("all tensors must be on the same device")
+    if x.dim() < 1 or w.dim() != 2 or w.shape[1] != x.shape[-1]:
+        raise ValueError(f"w must be [Nout, K] with K = x.shape[-1], got {tuple(w.shape)}")
+    K = x.shape[-1]
+    Nout = w.shape[0]
+    M = x.numel() // K if K else 0
+    out_shape = tuple(x.shape[:-1]) + (Nout,)
+    if bias is not None and tuple(bias.shape) != (Nout,):
+        raise ValueError(f"bias must be [{Nout}]")
+    if residual is not None and tuple(residual.shape) != out_shape:
+        raise ValueError(f"residual must be {out_shape}")
+    if out is None:
+        out = torch.empty(out_shape, dtype=dtype, device=x.device)
+    elif tuple(out.shape) != out_shape:
+        raise ValueError(f"out must be {out_shape}")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    flags = DTYPE_FP16 if dtype == torch.float16 else 0
+    rc = linear_raw(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                    residual.data_ptr() if residual is not None else None, out.data_ptr(), M, K,
+                    Nout, flags, stream.cuda_stream)
+    if rc != OK:
+        raise VitAttnError(rc, strerror(rc))
+    return out

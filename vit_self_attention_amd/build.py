@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libvitattn.so")
-SOURCES = [os.path.join(CSRC, "vitattn_fwd.hip"), os.path.join(CSRC, "vitattn_api.cpp")]
+SOURCES = [os.path.join(CSRC, "vitattn_fwd.hip"), os.path.join(CSRC, "vitattn_linear.hip"),
+           os.path.join(CSRC, "vitattn_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

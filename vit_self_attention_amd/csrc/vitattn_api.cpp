@@ -198,6 +198,40 @@ extern "C" int vitattn_plan_destroy(vitattn_plan plan) {
   return ok ? VITATTN_OK : VITATTN_ERR_GRAPH;
 }
 
+extern "C" int vitattn_linear(const void* x, const void* w, const void* bias, const void* residual,
+                              void* out, int M, int K, int Nout, int flags, void* stream) {
+  if ((flags & ~VITATTN_DTYPE_FP16) != 0) return VITATTN_ERR_BAD_LAYOUT;
+  if (M < 0 || K < 0 || Nout < 0) return VITATTN_ERR_BAD_SIZE;
+  if (K == 0 || K % 32 != 0 || Nout % 8 != 0) return VITATTN_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || Nout == 0) return VITATTN_OK;
+  if (!x || !w || !out) return VITATTN_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (bias && !aligned16(bias)) ||
+      (residual && !aligned16(residual)))
+    return VITATTN_ERR_MISALIGNED;
+  // the kernel addresses x and w rows with 32-bit byte offsets
+  const int64_t x_bytes = static_cast<int64_t>(M) * K * 2, w_bytes = static_cast<int64_t>(Nout) * K * 2;
+  if (x_bytes >= (int64_t(1) << 32) || w_bytes >= (int64_t(1) << 32)) return VITATTN_ERR_TOO_LARGE;
+  const int64_t o_bytes = static_cast<int64_t>(M) * Nout * 2;
+  if (o_bytes >= (int64_t(1) << 40)) return VITATTN_ERR_TOO_LARGE;
+  if (overlaps(out, o_bytes, x, x_bytes) || overlaps(out, o_bytes, w, w_bytes) ||
+      overlaps(out, o_bytes, bias, static_cast<int64_t>(Nout) * 2))
+    return VITATTN_ERR_OVERLAP;
+  // the residual may be the output itself (an in-place residual add: every
+  // element is read and written by the same lane), but not a shifted view
+  if (residual && residual != out && overlaps(out, o_bytes, residual, o_bytes)) return VITATTN_ERR_OVERLAP;
+  vitattn::LinearCall c{};
+  c.x = static_cast<const uint16_t*>(x);
+  c.w = static_cast<const uint16_t*>(w);
+  c.bias = static_cast<const uint16_t*>(bias);
+  c.residual = static_cast<const uint16_t*>(residual);
+  c.out = static_cast<uint16_t*>(out);
+  c.M = M;
+  c.K = K;
+  c.Nout = Nout;
+  c.f16 = (flags & VITATTN_DTYPE_FP16) != 0;
+  return vitattn::launch_linear(c, stream) == 0 ? VITATTN_OK : VITATTN_ERR_LAUNCH;
+}
+
 extern "C" const char* vitattn_strerror(int status) {
   switch (status) {
     case VITATTN_OK: return "success";
@@ -212,6 +246,8 @@ extern "C" const char* vitattn_strerror(int status) {
     case VITATTN_ERR_LAUNCH: return "kernel launch failed";
     case VITATTN_ERR_OVERLAP: return "out overlaps an input buffer";
     case VITATTN_ERR_GRAPH: return "recording or launching the HIP graph failed";
+    case VITATTN_ERR_UNSUPPORTED_SHAPE:
+      return "linear layer: K must be a positive multiple of 32 and Nout a multiple of 8";
     default: return "unknown status";
   }
 }

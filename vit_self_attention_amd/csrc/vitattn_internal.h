@@ -27,6 +27,23 @@ struct FwdArgs {
 // already validated.  Returns 0 or a negative VITATTN_ERR_* code.
 int launch_fwd(const FwdArgs& a, void* stream);
 
+// One linear layer: out[m][n] = sum_k x[m][k] * w[n][k] + bias[n]
+// (+ residual[m][n]); x [M][K], w [Nout][K], bias [Nout], residual and out
+// [M][Nout], all 16-bit.  Arguments are already validated (K a multiple of
+// 32, Nout a multiple of 8, byte offsets below 2^32).
+struct LinearCall {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* bias;      // NULL: no bias
+  const uint16_t* residual;  // NULL: no residual
+  uint16_t* out;
+  int M, K, Nout;
+  bool f16;
+};
+
+// Enqueues the linear kernel on `stream`.  Returns 0 or VITATTN_ERR_LAUNCH.
+int launch_linear(const LinearCall& c, void* stream);
+
 // Number of waves per workgroup the launcher picks for a problem (1, 2 or 4);
 // exposed for tests and the benchmark's reporting.
 int pick_waves(int B, int H, int N);
