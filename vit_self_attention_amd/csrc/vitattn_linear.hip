@@ -15,15 +15,18 @@
 // Work decomposition
 //   * one workgroup per BM x BN output tile; WM x WN waves, each owning a
 //     TM x TN sub-tile as (TN/32) x (TM/32) accumulators of the 32x32 MFMA;
-//   * the product is formed transposed, C^T = W X^T, so that every lane
-//     holds four consecutive output features of one token: the epilogue then
-//     reads bias and residual and writes the output 8 bytes at a time;
+//   * the product is formed transposed, C^T = W X^T (every lane holds runs
+//     of four consecutive output features of one token); the epilogue
+//     stages 32-token slabs through LDS as fp32 and writes whole 128-byte
+//     row segments, adding bias and residual on the way;
 //   * k in tiles of 32: x rows and w rows go direct to LDS (128-bit
-//     global_load_lds, no staging registers) into a three-stage ring, two
-//     tiles ahead, one barrier per tile.  LDS rows are 80 bytes (64 of data
-//     and a 16-byte slot that receives a copy and is never read): sixteen
-//     consecutive rows then fall in disjoint banks for the 128-bit operand
-//     reads;
+//     global_load_lds, no staging registers) into a four-stage ring, three
+//     tiles ahead, one barrier per tile.  An LDS row holds the tile's 64
+//     bytes of one x or w row as four 16-byte chunks, chunk c of row r at
+//     position c ^ ((r >> 2) & 3): sixteen consecutive rows read at one
+//     chunk then fall in sixteen distinct bank groups, with no padding;
+//   * operand reads for the next k step are issued before the MFMAs of the
+//     current one;
 //   * rows past M (or Nout) load row M-1 (Nout-1) and are never stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,12 +39,11 @@ namespace {
 typedef __bf16 lbf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 lf16x8 __attribute__((ext_vector_type(8)));
 typedef float lf32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t lu32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 32;         // k per tile
-constexpr int kRowElems = 40;   // LDS row stride in elements (80 bytes)
-constexpr int kSlotsRow = 5;    // 16-byte LDS slots per row (4 of data)
-constexpr int kStagesL = 3;
+constexpr int kRowElems = 32;   // LDS row stride in elements (64 bytes)
+constexpr int kSlotsRow = 4;    // 16-byte LDS slots per row
+constexpr int kStagesL = 4;
 
 struct LinearArgs {
   const uint16_t* x;
@@ -136,8 +138,9 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   const int ktiles = K / kBK;
 
   // this lane's 16-byte source chunk in fetch instruction i of this wave:
-  // slot s = I*64 + lane of the stage holds row s / 5, chunk s % 5 (chunk 4
-  // repeats chunk 3); rows < BM are x rows m0.., the rest w rows n0..
+  // slot s = I*64 + lane of the stage is position s % 4 of row s / 4, which
+  // holds chunk (s % 4) ^ ((row >> 2) & 3); rows < BM are x rows m0.., the
+  // rest w rows n0..
   const char* xg = reinterpret_cast<const char*>(a.x);
   const char* wg = reinterpret_cast<const char*>(a.w);
   uint32_t f_off[kPerWave];
@@ -146,8 +149,7 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
     const int I = i * NW + wave;
     const int s = I * 64 + lane;
     const int row = s / kSlotsRow;
-    int c = s - row * kSlotsRow;
-    c = c < 4 ? c : 3;
+    const int c = (s - row * kSlotsRow) ^ ((row >> 2) & 3);
     int r;
     if (row < BM) {
       r = m0 + row;
@@ -174,8 +176,10 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
 #define VITATTN_LWAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
     if (tiles_in_flight == 0) {
       VITATTN_LWAIT(0);
-    } else {
+    } else if (tiles_in_flight == 1) {
       VITATTN_LWAIT(kMinPerWave);
+    } else {
+      VITATTN_LWAIT(2 * kMinPerWave);
     }
 #undef VITATTN_LWAIT
     asm volatile("s_barrier" ::: "memory");
@@ -189,74 +193,106 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
-  // operand rows: A (w) rows wn*TN + 32j + col, B (x) rows wm*TM + 32i + col;
-  // k offset 8*half (+16 for the second k step)
-  const int a_off = (BM + wn * TN + col) * kRowElems + 8 * half;
-  const int b_off = (wm * TM + col) * kRowElems + 8 * half;
+  // operand rows: A (w) rows BM + wn*TN + 32j + col, B (x) rows
+  // wm*TM + 32i + col, both at k chunk 2*ks + half of the tile; the row bits
+  // that pick the chunk position are those of col (32j, 32i and the bases
+  // are multiples of 32)
+  const int swz = (col >> 2) & 3;
+  const int a_row = (BM + wn * TN + col) * kRowElems, b_row = (wm * TM + col) * kRowElems;
+  const int c_off0 = 8 * ((0 + half) ^ swz), c_off1 = 8 * ((2 + half) ^ swz);
 
-  fetch(0);
-  if (ktiles > 1) fetch(1);
-  wait_and_sync(ktiles > 1 ? 1 : 0);
+  const int pre = ktiles < kStagesL - 1 ? ktiles : kStagesL - 1;
+  for (int t = 0; t < pre; ++t) fetch(t);
+  wait_and_sync(pre - 1);
   for (int t = 0; t < ktiles; ++t) {
-    if (t + 2 < ktiles) fetch(t + 2);
+    if (t + kStagesL - 1 < ktiles) fetch(t + kStagesL - 1);
     const uint16_t* st = lds + (t % kStagesL) * kStageElems;
+    lbf16x8 av[2][FN], bv[2][FM];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      lbf16x8 av[FN], bv[FM];
+      const int co = ks ? c_off1 : c_off0;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        av[j] = *reinterpret_cast<const lbf16x8*>(st + a_off + 32 * j * kRowElems + 16 * ks);
+        av[ks][j] = *reinterpret_cast<const lbf16x8*>(st + a_row + 32 * j * kRowElems + co);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        bv[i] = *reinterpret_cast<const lbf16x8*>(st + b_off + 32 * i * kRowElems + 16 * ks);
+        bv[ks][i] = *reinterpret_cast<const lbf16x8*>(st + b_row + 32 * i * kRowElems + co);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] = lmma<kF16>(av[j], bv[i], acc[j][i]);
+        for (int i = 0; i < FM; ++i) acc[j][i] = lmma<kF16>(av[ks][j], bv[ks][i], acc[j][i]);
+    // tile t+1 must have landed (the tiles after it may stay in flight) and
+    // every wave must be done with stage t before it is refilled
+    if (t + 1 < ktiles) {
+      const int last = t + kStagesL - 1 < ktiles ? t + kStagesL - 1 : ktiles - 1;
+      wait_and_sync(last - (t + 1));
     }
-    // tile t+1 must have landed (t+2 may stay in flight) and every wave must
-    // be done with stage t before it is refilled with tile t+3
-    if (t + 1 < ktiles) wait_and_sync(t + 2 < ktiles ? 1 : 0);
   }
 
-  // ---- epilogue.  acc[j][i] is C^T for output features n0 + wn*TN + 32j +
-  // 8*(r/4) + 4*half + (r%4) and token m0 + wm*TM + 32i + col: each lane
-  // holds, per group g = r/4, four consecutive features of one token.
+  // ---- epilogue.  acc[j][i][r] is C^T for output feature
+  // n0 + wn*TN + 32j + 8*(r/4) + 4*half + (r%4) and token m0 + wm*TM + 32i +
+  // col.  Each 32-token slab i of the wave's tile goes through the wave's
+  // own LDS region as fp32 (the ring is free once every wave has left the
+  // loop), and comes back as rows: lane l then holds 8 consecutive features
+  // of one token, adds bias and residual and writes 16 bytes, eight lanes
+  // covering one 128-byte row segment.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int kSlabStride = TN + 4;  // floats per staged row (272 bytes for TN = 64)
+  static_assert(NW * 32 * kSlabStride * 4 <= kStagesL * kStageElems * 2, "staging fits in the ring");
+  static_assert(TN == 64, "eight lanes of 8 features per staged row");
+  float* slab = reinterpret_cast<float*>(lds) + wave * 32 * kSlabStride;
+  const int rrow = lane >> 3, rch = lane & 7;       // read-back: row within 8, 8-feature chunk
+  const int n = n0 + wn * TN + 8 * rch;
+  float bsum[8];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
+  for (int e = 0; e < 8; ++e) bsum[e] = 0.f;
+  if (a.bias && n < Nout) {
+    const uint4 bb = *reinterpret_cast<const uint4*>(a.bias + n);
+    const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = n0 + wn * TN + 32 * j + 8 * g + 4 * half;
-      if (n >= Nout) continue;  // Nout is a multiple of 8: all four or none
-      float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-      if (a.bias) {
-        const lu32x2 bb = *reinterpret_cast<const lu32x2*>(a.bias + n);
-        bsum[0] = widen16<kF16>(bb[0] & 0xffffu);
-        bsum[1] = widen16<kF16>(bb[0] >> 16);
-        bsum[2] = widen16<kF16>(bb[1] & 0xffffu);
-        bsum[3] = widen16<kF16>(bb[1] >> 16);
+    for (int e = 0; e < 4; ++e) {
+      bsum[2 * e] = widen16<kF16>(bw[e] & 0xffffu);
+      bsum[2 * e + 1] = widen16<kF16>(bw[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+        *reinterpret_cast<float4*>(slab + col * kSlabStride + 32 * j + 8 * g + 4 * half) = v;
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * TM + 32 * i + col;
-        if (m >= M) continue;
-        const int64_t o = static_cast<int64_t>(m) * Nout + n;
-        float v0 = acc[j][i][4 * g + 0] + bsum[0];
-        float v1 = acc[j][i][4 * g + 1] + bsum[1];
-        float v2 = acc[j][i][4 * g + 2] + bsum[2];
-        float v3 = acc[j][i][4 * g + 3] + bsum[3];
-        if (a.residual) {
-          const lu32x2 rr = *reinterpret_cast<const lu32x2*>(a.residual + o);
-          v0 += widen16<kF16>(rr[0] & 0xffffu);
-          v1 += widen16<kF16>(rr[0] >> 16);
-          v2 += widen16<kF16>(rr[1] & 0xffffu);
-          v3 += widen16<kF16>(rr[1] >> 16);
+    for (int q = 0; q < 4; ++q) {
+      const int row = 8 * q + rrow;
+      const float4 lo = *reinterpret_cast<const float4*>(slab + row * kSlabStride + 8 * rch);
+      const float4 hi = *reinterpret_cast<const float4*>(slab + row * kSlabStride + 8 * rch + 4);
+      const int m = m0 + wm * TM + 32 * i + row;
+      if (m >= M || n >= Nout) continue;
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += bsum[e];
+      const int64_t o = static_cast<int64_t>(m) * Nout + n;
+      if (a.residual) {
+        const uint4 rr = *reinterpret_cast<const uint4*>(a.residual + o);
+        const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] += widen16<kF16>(rw[e] & 0xffffu);
+          v[2 * e + 1] += widen16<kF16>(rw[e] >> 16);
         }
-        lu32x2 w;
-        w[0] = pack16x2<kF16>(v0, v1);
-        w[1] = pack16x2<kF16>(v2, v3);
-        *reinterpret_cast<lu32x2*>(a.out + o) = w;
       }
+      uint4 w;
+      w.x = pack16x2<kF16>(v[0], v[1]);
+      w.y = pack16x2<kF16>(v[2], v[3]);
+      w.z = pack16x2<kF16>(v[4], v[5]);
+      w.w = pack16x2<kF16>(v[6], v[7]);
+      *reinterpret_cast<uint4*>(a.out + o) = w;
     }
   }
 }
