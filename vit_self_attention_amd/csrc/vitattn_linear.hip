@@ -21,12 +21,13 @@
 //     row segments, adding bias and residual on the way;
 //   * k in tiles of 32: x rows and w rows go direct to LDS (128-bit
 //     global_load_lds, no staging registers) into a four-stage ring, three
-//     tiles ahead, one barrier per tile.  An LDS row holds the tile's 64
+//     tiles ahead, one barrier per tile, waited for two tiles ahead.  An LDS row holds the tile's 64
 //     bytes of one x or w row as four 16-byte chunks, chunk c of row r at
 //     position c ^ ((r >> 2) & 3): sixteen consecutive rows read at one
 //     chunk then fall in sixteen distinct bank groups, with no padding;
 //   * operand reads for the next k step are issued before the MFMAs of the
-//     current one;
+//     current one, and those of the next tile's first step before the
+//     barrier that ends a tile (its data was published one barrier earlier);
 //   * rows past M (or Nout) load row M-1 (Nout-1) and are never stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -201,34 +202,52 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   const int a_row = (BM + wn * TN + col) * kRowElems, b_row = (wm * TM + col) * kRowElems;
   const int c_off0 = 8 * ((0 + half) ^ swz), c_off1 = 8 * ((2 + half) ^ swz);
 
+  // operands of one k step (ks = 0, 1) of the tile in stage `st`
+  auto load_ops = [&](const uint16_t* st, int ks, lbf16x8* av, lbf16x8* bv) __attribute__((always_inline)) {
+    const int co = ks ? c_off1 : c_off0;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) av[j] = *reinterpret_cast<const lbf16x8*>(st + a_row + 32 * j * kRowElems + co);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) bv[i] = *reinterpret_cast<const lbf16x8*>(st + b_row + 32 * i * kRowElems + co);
+  };
+  // tiles fetched after tile t (0 .. kStagesL-2) when the fetch of tile
+  // `last` is the most recent
+  auto in_flight_after = [&](int t, int last) { return last > t ? last - t : 0; };
+
+  // Schedule: the fetch of tile t+3 is issued at the top of tile t; at the
+  // end of tile t each wave waits for its part of tile t+2, reads the first
+  // k step of tile t+1 (complete and visible since the previous barrier)
+  // and meets the others.  The barrier both publishes tile t+2 and frees
+  // stage t for the fetch of tile t+4.
   const int pre = ktiles < kStagesL - 1 ? ktiles : kStagesL - 1;
   for (int t = 0; t < pre; ++t) fetch(t);
-  wait_and_sync(pre - 1);
+  wait_and_sync(in_flight_after(1, pre - 1));  // tiles 0 and 1 landed
+  lbf16x8 a0[FN], b0[FM], a1[FN], b1[FM];
+  load_ops(lds, 0, a0, b0);
   for (int t = 0; t < ktiles; ++t) {
     if (t + kStagesL - 1 < ktiles) fetch(t + kStagesL - 1);
     const uint16_t* st = lds + (t % kStagesL) * kStageElems;
-    lbf16x8 av[2][FN], bv[2][FM];
+    load_ops(st, 1, a1, b1);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int co = ks ? c_off1 : c_off0;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        av[ks][j] = *reinterpret_cast<const lbf16x8*>(st + a_row + 32 * j * kRowElems + co);
+      for (int i = 0; i < FM; ++i) acc[j][i] = lmma<kF16>(a0[j], b0[i], acc[j][i]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        bv[ks][i] = *reinterpret_cast<const lbf16x8*>(st + b_row + 32 * i * kRowElems + co);
-    }
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] = lmma<kF16>(av[ks][j], bv[ks][i], acc[j][i]);
-    // tile t+1 must have landed (the tiles after it may stay in flight) and
-    // every wave must be done with stage t before it is refilled
+      for (int i = 0; i < FM; ++i) acc[j][i] = lmma<kF16>(a1[j], b1[i], acc[j][i]);
     if (t + 1 < ktiles) {
       const int last = t + kStagesL - 1 < ktiles ? t + kStagesL - 1 : ktiles - 1;
-      wait_and_sync(last - (t + 1));
+      asm volatile("" ::: "memory");
+#define VITATTN_LWAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+      if (in_flight_after(t + 2, last) == 0) {
+        VITATTN_LWAIT(0);
+      } else {
+        VITATTN_LWAIT(kMinPerWave);
+      }
+#undef VITATTN_LWAIT
+      load_ops(lds + ((t + 1) % kStagesL) * kStageElems, 0, a0, b0);
+      asm volatile("s_barrier" ::: "memory");
     }
   }
 
