@@ -54,6 +54,9 @@ def _parse():
                    help="CPU time budget for the oracle baseline")
     p.add_argument("--fmt", choices=["bf16", "f16"], default="bf16",
                    help="element format of inputs and output (f16: the fp16 variant)")
+    p.add_argument("--linear-only", nargs="?", const="all", default=None, metavar="NAME",
+                   help="only the linear-layer figures, or only figure NAME (qkv_224x2, "
+                        "qkv_384x48, proj_384x48): a short run, for counter profiles")
     p.add_argument("--sweep", action="store_true",
                    help="per-workload statistics for all workloads (one JSON line)")
     p.add_argument("--samples", type=int, default=50, help="samples per workload in --sweep")
@@ -107,6 +110,24 @@ def _device_inputs(wl, device, layers):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vitattn_fwd_hbm_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "vit_self_attention_amd", "csrc", "vitattn_fwd.hip")
+LINEAR_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vitattn_linear_hbm_traffic.json")
+LINEAR_SOURCE = os.path.join(ROOT, "vit_self_attention_amd", "csrc", "vitattn_linear.hip")
+
+
+def _linear_traffic(name):
+    """HBM bytes per call of the linear kernel for figure `name` from the
+    committed counter runs, or None once the kernel source has changed."""
+    import hashlib
+    try:
+        with open(LINEAR_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(LINEAR_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha or name not in rec.get("calls", {}):
+        return None
+    return rec["calls"][name]["bytes_per_call"]
 
 
 def _measured_traffic(wl):
@@ -297,11 +318,12 @@ def _mfma_probe(stream):
     return res
 
 
-def _linear_figures(stream, steps=20):
+def _linear_figures(stream, steps=10, only=None):
     """The qkv projection and the output projection (bias + residual) of
     SigLIP-So400m (1152 -> 3456 and 1152 -> 1152) at 224 px x 2 and 384 px
-    x 48, through vitattn_linear: time per call (HIP events over `steps`
-    back-to-back calls after 3), TFLOP/s, roofline, and parity of sampled
+    x 48, through vitattn_linear: time per call (median of 3 batches of
+    `steps` back-to-back calls between HIP events, after a warmup of at
+    least ~5 ms of kernel time), TFLOP/s, roofline, and parity of sampled
     rows with the fp64 oracle."""
     import numpy as np
     import torch
@@ -315,6 +337,8 @@ def _linear_figures(stream, steps=20):
     for name, M, Nout, resid in (("qkv_224x2", 2 * 256, 3456, False),
                                  ("qkv_384x48", 48 * 729, 3456, False),
                                  ("proj_384x48", 48 * 729, 1152, True)):
+        if only is not None and name != only:
+            continue
         K = 1152
         x = f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
         w = f32_to_bf16_bits(rng.standard_normal((Nout, K)).astype(np.float32) / np.float32(34.0))
@@ -326,17 +350,22 @@ def _linear_figures(stream, steps=20):
 
         xd, wd, bd, rd = dv(x), dv(w), dv(b), dv(r)
         out = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+        # warm up for at least ~5 ms of kernel time (the clocks ramp up after
+        # the CPU-only oracle leg), then the median of 3 batches
+        for _ in range(max(3, min(30, int(5e-3 * 1e15 / (2.0 * M * K * Nout))))):
+            va.linear(xd, wd, bd, rd, out=out, stream=stream)
+        torch.cuda.synchronize()
+        batches = []
         for _ in range(3):
-            va.linear(xd, wd, bd, rd, out=out, stream=stream)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(steps):
-            va.linear(xd, wd, bd, rd, out=out, stream=stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        us = t0.elapsed_time(t1) * 1e3 / steps
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(steps):
+                va.linear(xd, wd, bd, rd, out=out, stream=stream)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            batches.append(t0.elapsed_time(t1) * 1e3 / steps)
+        us = sorted(batches)[1]
         flops = 2.0 * M * K * Nout
         tf = flops / (us * 1e-6) / 1e12
         nbytes = 2.0 * (M * K + Nout * K + M * Nout * (2 if resid else 1) + Nout)
@@ -345,7 +374,8 @@ def _linear_figures(stream, steps=20):
         ref = lo.linear_rows(x, w, b, r, rows)
         err = np.abs(got - ref)
         res[name] = {"M": M, "K": K, "Nout": Nout, "bias": True, "residual": resid,
-                     "us_per_call": us, "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
+                     "us_per_call": us, "batches_us_per_call": batches,
+                     "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
                      "roofline": {"bound": "mfma" if flops / nbytes >= RIDGE else "hbm",
                                   "achieved": tf if flops / nbytes >= RIDGE else nbytes / (us * 1e-6) / 1e9,
                                   "peak": PEAK_BF16_TFLOPS if flops / nbytes >= RIDGE else PEAK_HBM_GBPS,
@@ -354,6 +384,8 @@ def _linear_figures(stream, steps=20):
                      "sampled_rows_max_rel_err": float((err / (np.abs(ref) + 1e-3)).max())}
         r_ = res[name]["roofline"]
         r_["frac"] = r_["achieved"] / r_["peak"]
+        r_["traffic"] = _linear_traffic(name)
+        res[name]["algorithmic_bytes"] = nbytes
         del xd, wd, bd, rd, out
     torch.cuda.empty_cache()
     return res
@@ -411,6 +443,13 @@ def main():
         return
     if args.sweep:
         _sweep(args)
+        return
+    if args.linear_only:
+        import torch
+        torch.cuda.set_device(0)
+        only = None if args.linear_only == "all" else args.linear_only
+        print(json.dumps({"linear": _linear_figures(torch.cuda.current_stream(), steps=2, only=only)}),
+              flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "

@@ -132,8 +132,17 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   const int col = lane & 31, half = lane >> 5;
 
+  // Tile order: each XCD takes a contiguous range of tiles (lxcd_remap),
+  // and within it tiles run in groups of kGroupM token blocks, output
+  // feature blocks slowest inside a group, so the workgroups resident in an
+  // XCD at one time share both x and w rows in its L2.
+  constexpr int kGroupM = 8;
   const int tile = lxcd_remap(blockIdx.x, gridDim.x);
-  const int mb = tile / a.nblocks, nb = tile - mb * a.nblocks;
+  const int per_group = kGroupM * a.nblocks;
+  const int first_m = (tile / per_group) * kGroupM;
+  const int gsize = a.mblocks - first_m < kGroupM ? a.mblocks - first_m : kGroupM;
+  const int within = tile - (tile / per_group) * per_group;
+  const int mb = first_m + within % gsize, nb = within / gsize;
   const int m0 = mb * BM, n0 = nb * BN;
   const int M = a.M, K = a.K, Nout = a.Nout;
   const int ktiles = K / kBK;
