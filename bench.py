@@ -523,11 +523,11 @@ def main():
     if not args.no_target and wl.key != "c5":
         t = WORKLOADS["c5"]
         tins, touts, _ = _device_inputs(t, device, 1)
-        # 30 warmup launches (about 6 ms: the clocks settle after the idle
+        # 100 warmup launches (about 20 ms: the clocks settle after the idle
         # CPU leg), then 3 timed batches of 30; the median batch is reported
         batches = []
         for i in range(3):
-            t_ms, _ = _time_steps(va, t, tins, touts, 30, 30 if i == 0 else 0, stream)
+            t_ms, _ = _time_steps(va, t, tins, touts, 30, 100 if i == 0 else 0, stream)
             batches.append(t_ms * 1e3 / 30)
         us = sorted(batches)[1]
         tf = t.flops_per_layer / (us * 1e-6) / 1e12
@@ -539,7 +539,7 @@ def main():
             "batches_us_per_layer": batches,
             "frac_of_measured_random_operand_mfma": tf / probe["random_operands_tflops"],
             "timing": "median of 3 batches of 30 back-to-back launches, each between two HIP "
-                      "events on the launch stream, after 30 warmup launches"}
+                      "events on the launch stream, after 100 warmup launches"}
         del tins, touts
 
     print(json.dumps(result), flush=True)
