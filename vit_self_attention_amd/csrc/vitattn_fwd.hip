@@ -75,10 +75,10 @@ struct KernelArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  int64_t q_sb, q_sh, q_st;
-  int64_t k_sb, k_sh, k_st;
-  int64_t v_sb, v_sh, v_st;
-  int64_t o_sb, o_sh, o_st;
+  // strides in elements; Q, K and V share theirs (both layouts)
+  int64_t i_sb, i_sh;
+  int64_t o_sb, o_sh;
+  int i_st, o_st;  // token strides (a 64-token tile spans < 2 GiB)
   int H, N;
   int qblocks;     // query blocks per (image, head)
   int items;       // B * H * qblocks work items (image, head, query block)
@@ -306,8 +306,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   };
   int b, h, qb;
   coords(it0, b, h, qb);
-  const uint16_t* kbase = a.k + b * a.k_sb + h * a.k_sh;
-  const uint16_t* vbase = a.v + b * a.v_sb + h * a.v_sh;
+  const uint16_t* kbase = a.k + b * a.i_sb + h * a.i_sh;
+  const uint16_t* vbase = a.v + b * a.i_sb + h * a.i_sh;
 
   // ---- constant tail of each V row (D = 72): d = 72 holds 1, d = 73..79
   // hold 0.  Every wave writes the whole column of a stage itself (lane =
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   auto load_q = [&](int b_, int h_, int qb_, bf16x8* dq, bf16x4& dqt) __attribute__((always_inline)) {
     const int q_ = first_query(qb_) + col;
     const int qi_ = q_ < N ? q_ : N - 1;
-    const uint16_t* qrow = a.q + b_ * a.q_sb + h_ * a.q_sh + static_cast<int64_t>(qi_) * a.q_st;
+    const uint16_t* qrow = a.q + b_ * a.i_sb + h_ * a.i_sh + static_cast<int64_t>(qi_) * a.i_st;
 #pragma unroll
     for (int s = 0; s < 4; ++s) dq[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * half);
     if constexpr (D == 72) dqt = *reinterpret_cast<const bf16x4*>(qrow + 64 + 4 * half);
@@ -354,9 +354,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     const int qn0 = first_query(nqb);
     const int qlo = qn0 < N ? qn0 : N - 1;
     const int r = qn0 + col < N ? qn0 + col : N - 1;
-    const char* base = reinterpret_cast<const char*>(a.q + nb * a.q_sb + nh * a.q_sh +
-                                                     static_cast<int64_t>(qlo) * a.q_st);
-    const uint32_t off = static_cast<uint32_t>((r - qlo) * a.q_st * 2 + (2 * D - 16) * half);
+    const char* base = reinterpret_cast<const char*>(a.q + nb * a.i_sb + nh * a.i_sh +
+                                                     static_cast<int64_t>(qlo) * a.i_st);
+    const uint32_t off = static_cast<uint32_t>((r - qlo) * a.i_st * 2 + (2 * D - 16) * half);
     dma16(base, off, lds_base + 2 * kStages * kStageElems);
   };
 
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // 16-byte column s % slots_per_row (clamped to the last chunk of D).  In
   // the last tile, rows past N repeat row N-1 (finite data that a zero
   // weight removes).
-  const int k_st32 = static_cast<int>(a.k_st), v_st32 = static_cast<int>(a.v_st);
+  const int st32 = a.i_st;
   // row and clamped 16-byte column of this lane's slot in fetch instruction I
   auto slot_rc = [&](int I, int& row, int& cc) __attribute__((always_inline)) {
     const bool is_k = I < kKInstr;
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     const int I = i * NW + wave;
     int row, cc;
     slot_rc(I, row, cc);
-    f_off[i] = static_cast<uint32_t>((row * (I < kKInstr ? k_st32 : v_st32) + cc * 8) * 2);
+    f_off[i] = static_cast<uint32_t>((row * st32 + cc * 8) * 2);
   }
   // issues this wave's fetch instructions for key tile t of the (image,
   // head) whose K and V start at kb_ptr and vb_ptr, into LDS stage `st`, as
@@ -391,8 +391,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   auto fetch_tile_at = [&](const uint16_t* kb_ptr, const uint16_t* vb_ptr, int t, int st)
                            __attribute__((always_inline)) {
     const int kb = t * kBlockN;
-    const char* gk = reinterpret_cast<const char*>(kb_ptr + static_cast<int64_t>(kb) * a.k_st);
-    const char* gv = reinterpret_cast<const char*>(vb_ptr + static_cast<int64_t>(kb) * a.v_st);
+    const char* gk = reinterpret_cast<const char*>(kb_ptr + static_cast<int64_t>(kb) * a.i_st);
+    const char* gv = reinterpret_cast<const char*>(vb_ptr + static_cast<int64_t>(kb) * a.i_st);
     const uint32_t stage = lds_base + 2 * st * kStageElems;
     auto slot_addr = [&](int I) {
       return stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512);
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         int row, cc;
         slot_rc(I, row, cc);
         const int r = row < last ? row : last;
-        dma16(is_k ? gk : gv, static_cast<uint32_t>((r * (is_k ? k_st32 : v_st32) + cc * 8) * 2), slot_addr(I));
+        dma16(is_k ? gk : gv, static_cast<uint32_t>((r * st32 + cc * 8) * 2), slot_addr(I));
       }
     }
   };
@@ -435,8 +435,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       ++f_r;
       int bn, hn, qn;
       coords(item_at(f_r), bn, hn, qn);
-      f_kb = a.k + bn * a.k_sb + hn * a.k_sh;
-      f_vb = a.v + bn * a.v_sb + hn * a.v_sh;
+      f_kb = a.k + bn * a.i_sb + hn * a.i_sh;
+      f_vb = a.v + bn * a.i_sb + hn * a.i_sh;
     }
   };
   // Waits until the fetches of all but the last `tiles_in_flight` (0 or 1)
@@ -655,7 +655,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
         } else if constexpr (kNext) {
           const int ii = i - kHalfPv;
 #pragma unroll
-          for (int g = 8 * ii / kHalfPv; g < 8 * (ii + 1) / kHalfPv; ++g) gmax = fmaxf(gmax, max4(nxt, g));
+          for (int g = 8 * ii / kHalfPv; g < 8 * (ii + 1) / kHalfPv; ++g) {
+            // two three-input maxima per group of four logits
+            const f32x16& v = nxt[g >> 2];
+            const int r = 4 * (g & 3);
+            gmax = fmaxf(fmaxf(gmax, v[r]), v[r + 1]);
+            gmax = fmaxf(fmaxf(gmax, v[r + 2]), v[r + 3]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -933,10 +939,18 @@ int launch_fwd(const FwdArgs& f, void* stream) {
   ka.k = f.k;
   ka.v = f.v;
   ka.o = f.o;
-  ka.q_sb = f.q_sb; ka.q_sh = f.q_sh; ka.q_st = f.q_st;
-  ka.k_sb = f.k_sb; ka.k_sh = f.k_sh; ka.k_st = f.k_st;
-  ka.v_sb = f.v_sb; ka.v_sh = f.v_sh; ka.v_st = f.v_st;
-  ka.o_sb = f.o_sb; ka.o_sh = f.o_sh; ka.o_st = f.o_st;
+  // Q, K and V share strides in both layouts, and a 64-token tile spans
+  // less than 2 GiB (both checked by the caller)
+  if (f.k_sb != f.q_sb || f.v_sb != f.q_sb || f.k_sh != f.q_sh || f.v_sh != f.q_sh ||
+      f.k_st != f.q_st || f.v_st != f.q_st || 64 * f.q_st >= (int64_t(1) << 30) ||
+      64 * f.o_st >= (int64_t(1) << 30))
+    return VITATTN_ERR_LAUNCH;
+  ka.i_sb = f.q_sb;
+  ka.i_sh = f.q_sh;
+  ka.i_st = static_cast<int>(f.q_st);
+  ka.o_sb = f.o_sb;
+  ka.o_sh = f.o_sh;
+  ka.o_st = static_cast<int>(f.o_st);
   ka.H = f.H;
   ka.N = f.N;
   // A zero scale would turn masked (-inf) logits into NaN; any scale below
