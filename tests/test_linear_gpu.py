@@ -153,3 +153,34 @@ def test_binding_rejects_bad_shapes(dev, va):
     with pytest.raises(va.VitAttnError):
         va.linear(torch.zeros((4, 48), dtype=torch.bfloat16, device=dev),
                   torch.zeros((8, 48), dtype=torch.bfloat16, device=dev))
+
+
+def test_attention_sublayer_composition(dev, va):
+    """The attention sublayer of a SigLIP block on the library's kernels:
+    qkv = x Wqkv^T + b (vitattn_linear), viewed as the packed [B,N,3,H,D]
+    input of vitattn_fwd, whose [B,N,H,D] output viewed as [B,N,H*D] feeds
+    the output projection with bias and the residual x.  Each stage is
+    checked against the oracle on exactly the bits the GPU stage consumed."""
+    import math
+    import torch
+    import oracle
+    B, N, H, D = 2, 256, 16, 72
+    E = H * D
+    rng = np.random.default_rng(40)
+    x = ROUND["bf16"](rng.standard_normal((B * N, E)).astype(np.float32))
+    wqkv = ROUND["bf16"](rng.standard_normal((3 * E, E)).astype(np.float32) * np.float32(1 / math.sqrt(E)))
+    bqkv = ROUND["bf16"](rng.standard_normal(3 * E).astype(np.float32) * np.float32(0.1))
+    wo = ROUND["bf16"](rng.standard_normal((E, E)).astype(np.float32) * np.float32(1 / math.sqrt(E)))
+    bo = ROUND["bf16"](rng.standard_normal(E).astype(np.float32) * np.float32(0.1))
+    xd = _dev(x, "bf16", dev)
+    qkv = va.linear(xd, _dev(wqkv, "bf16", dev), _dev(bqkv, "bf16", dev))
+    o = va.fwd(qkv.view(B, N, 3, H, D), scale=1 / math.sqrt(D))
+    y = va.linear(o.view(B * N, E), _dev(wo, "bf16", dev), _dev(bo, "bf16", dev), residual=xd)
+    torch.cuda.synchronize(dev)
+    qkv_bits, o_bits, y_bits = _host(qkv), _host(o), _host(y)
+    _check(qkv_bits, x, wqkv, bqkv, None, "bf16", what="sublayer qkv")
+    ref_o = oracle.attention(qkv_bits.reshape(B, N, 3, H, D), None, None, 1, B, H, N, D, 1 / math.sqrt(D))
+    err = np.abs(lo.widen(o_bits).reshape(B, N, H, D) - ref_o)
+    print(f"sublayer attention: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    _check(y_bits, o_bits.reshape(B * N, E), wo, bo, x, "bf16", what="sublayer proj + residual")
