@@ -410,7 +410,14 @@ def _cpu_baseline(wl, host, budget_s):
         done += 1
     dt = time.perf_counter() - t0
     tflops = wl.flops_per_layer * done / dt / 1e12
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{done} layer calls of the timed workload ({done / len(host):.2f} steps) "
                       f"in {dt:.1f} s, fp64, C + OpenMP",
             "ms_per_layer": dt / done * 1e3}, refs
