@@ -14,7 +14,9 @@
 //
 // Work decomposition
 //   * one workgroup per BM x BN output tile; WM x WN waves, each owning a
-//     TM x TN sub-tile as (TN/32) x (TM/32) accumulators of the 32x32 MFMA;
+//     TM x TN sub-tile as (TN/32) x (TM/32) accumulators of the 32x32 MFMA
+//     (256 x 256, 128 x 128 or 64 x 128 tiles, the largest that still give
+//     one workgroup per compute unit);
 //   * the product is formed transposed, C^T = W X^T (every lane holds runs
 //     of four consecutive output features of one token); the epilogue
 //     stages 32-token slabs through LDS as fp32 and writes whole 128-byte
@@ -339,11 +341,15 @@ int launch_linear_cfg(const LinearArgs& la0, hipStream_t s) {
 
 template <bool kF16>
 int launch_linear_typed(const LinearArgs& la, hipStream_t s) {
-  // 256 x 256 tiles (eight waves of 128 x 64) when they still give a few
-  // hundred workgroups; 128 x 128 tiles (four waves of 64 x 64) otherwise
-  const int64_t big = static_cast<int64_t>((la.M + 255) / 256) * ((la.Nout + 255) / 256);
-  if (big >= 256) return launch_linear_cfg<2, 4, 128, 64, kF16>(la, s);
-  return launch_linear_cfg<2, 2, 64, 64, kF16>(la, s);
+  // the largest tiles that still give a workgroup per compute unit (256 on
+  // MI355X): 256 x 256 (eight waves of 128 x 64), 128 x 128 (four waves of
+  // 64 x 64), else 64 x 128 (four waves of 32 x 64)
+  auto tiles = [&](int bm, int bn) {
+    return static_cast<int64_t>((la.M + bm - 1) / bm) * ((la.Nout + bn - 1) / bn);
+  };
+  if (tiles(256, 256) >= 256) return launch_linear_cfg<2, 4, 128, 64, kF16>(la, s);
+  if (tiles(128, 128) >= 256) return launch_linear_cfg<2, 2, 64, 64, kF16>(la, s);
+  return launch_linear_cfg<2, 2, 32, 64, kF16>(la, s);
 }
 
 }  // namespace
