@@ -143,3 +143,48 @@ def test_plan_argument_errors(dev, va):
         va.Plan([calls[1], short])  # every call must have the same shape
     with pytest.raises(ValueError):
         va.Plan(calls, outs=[torch.empty(1, device=dev, dtype=torch.bfloat16)] * 2)
+
+
+def test_sublayer_captured_by_torch_graph(dev, va):
+    """Every entry point is capturable: the attention sublayer (qkv
+    projection, attention, output projection with residual) recorded with
+    torch.cuda.CUDAGraph and replayed three times, with eager work and
+    synchronisations in between, matches the eager calls bitwise each time."""
+    import math
+    import torch
+    torch.manual_seed(3)
+    B, N, H, D = 2, 256, 16, 72
+    E = H * D
+    x = torch.randn(B, N, E, device=dev).to(torch.bfloat16)
+    wqkv = (torch.randn(3 * E, E, device=dev) / math.sqrt(E)).to(torch.bfloat16)
+    bqkv = (torch.randn(3 * E, device=dev) * 0.1).to(torch.bfloat16)
+    wo = (torch.randn(E, E, device=dev) / math.sqrt(E)).to(torch.bfloat16)
+    bo = (torch.randn(E, device=dev) * 0.1).to(torch.bfloat16)
+    qkv = torch.empty(B, N, 3 * E, device=dev, dtype=torch.bfloat16)
+    o = torch.empty(B, N, H, D, device=dev, dtype=torch.bfloat16)
+    y = torch.empty(B, N, E, device=dev, dtype=torch.bfloat16)
+
+    def sublayer():
+        va.linear(x, wqkv, bqkv, out=qkv)
+        va.fwd(qkv.view(B, N, 3, H, D), out=o)
+        va.linear(o.view(B, N, E), wo, bo, residual=x, out=y)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        sublayer()  # warm up on the capture stream
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    want = bits_of(y)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sublayer()
+    for _ in range(3):
+        y.zero_()
+        qkv.zero_()
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        assert np.array_equal(bits_of(y), want)
+        sublayer()  # eager work between replays
+        torch.cuda.synchronize(dev)
+        assert np.array_equal(bits_of(y), want)
