@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "vitattn.h"
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // conflicts and runs about 1.2 times faster: the last rounds, past
   // 0.9 times the average number of items, go to those workgroups only.
   // (The host loops only with at least two items per workgroup.)
-  int it0 = 0, lo = 0, hi = 0, gx = 1, ky = 1, lx = 0;
+  int it0 = 0, lo = 0, gx = 1, ky = 1, lx = 0;
   bool single = true;
   int nitems = 1;
   if (a.grid >= a.items) {
@@ -283,7 +284,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     const int per = a.items >> 3, rem = a.items & 7;
     lo = x * per + (x < rem ? x : rem);
     const int nx = per + (x < rem ? 1 : 0);
-    hi = lo + nx;
     ky = (9 * nx + 5 * gx) / (10 * gx);  // 0.9 * nx / gx, rounded, at most nx / gx
     if (ky > nx / gx) ky = nx / gx;
     it0 = lo + lx;
@@ -298,11 +298,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     if (single) return it0;
     return r < ky ? lo + r * gx + lx : lo + ky * gx + (r - ky) * (gx / 2) + lx;
   };
-  auto coords = [&](int item, int& bi, int& hi, int& qbi) {
+  auto coords = [&](int item, int& bi, int& hi_, int& qbi) {
     const int bh = item / a.qblocks;
     qbi = item - bh * a.qblocks;
     bi = bh / a.H;
-    hi = bh - bi * a.H;
+    hi_ = bh - bi * a.H;
   };
   int b, h, qb;
   coords(it0, b, h, qb);
@@ -890,11 +890,15 @@ namespace {
 int compute_units() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  static int cache[64] = {0};
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  // several host threads may launch at once: the cache entries are atomic
+  static std::atomic<int> cache[64];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
