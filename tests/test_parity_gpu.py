@@ -88,6 +88,37 @@ def test_grid_shapes(dev, va, B, H, N):
     assert_parity(got, _oracle(li, LAYOUT_PACKED, wl.scale), f"grid B={B} H={H} N={N}")
 
 
+@pytest.mark.parametrize("D", [64, 72])
+def test_long_sequence_looping_workgroups(dev, va, D):
+    """N = 2048 with enough (image, head, query block) items for the
+    looping-workgroup kernel (B*H*16 = 1024 items), full comparison: long
+    tile streams, many items per workgroup, lazy rescales across 32 tiles."""
+    wl = Workload("t", "long", B=4, N=2048, H=16, D=D, layout=LAYOUT_PACKED, layers=1,
+                  kind="stress", index=70 + D)
+    li = make_layer(wl, 0)
+    got = run_gpu(li, LAYOUT_PACKED, wl.scale, dev)
+    assert_parity(got, _oracle(li, LAYOUT_PACKED, wl.scale), f"long N=2048 D={D}")
+
+
+def test_separate_layout_full_size_sampled_rows(dev, va):
+    """The 384 px workload's shape and values in the separate [B,H,N,D]
+    layout, run by the looping-workgroup kernel, checked on 256 sampled
+    (image, head, query) rows, including the ragged last query block."""
+    wl = WORKLOADS["c5"]
+    li = make_layer(wl, 0)
+    B, N, H, D = li.q.shape
+    arrs = li.in_layout(LAYOUT_SEPARATE)
+    got = run_gpu(li, LAYOUT_SEPARATE, wl.scale, dev)
+    rng = np.random.default_rng(71)
+    rows = np.stack([rng.integers(0, B, 256), rng.integers(0, H, 256), rng.integers(0, N, 256)], 1)
+    rows[:8, 2] = [0, 1, 127, 128, 639, 640, 727, 728]
+    ref = oracle.attention_rows(*arrs, LAYOUT_SEPARATE, B, H, N, D, wl.scale, rows)
+    got_rows = np.stack([got[b, i, h] for b, h, i in rows])
+    err = np.abs(got_rows - ref)
+    print(f"separate c5 sampled: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
 # ---------------------------------------------------------------- special cases
 
 def _rand(rng, shape, std=1.0):
