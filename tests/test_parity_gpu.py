@@ -78,9 +78,12 @@ def test_stress_logits_parity(dev, va, N, D):
     assert_parity(got, _oracle(li, LAYOUT_PACKED, wl.scale), f"stress N={N} D={D}")
 
 
-@pytest.mark.parametrize("B,H,N", [(1, 1, 729), (4, 16, 729), (96, 16, 64), (1, 48, 129)])
+@pytest.mark.parametrize("B,H,N", [(1, 1, 729), (4, 16, 729), (96, 16, 64), (1, 48, 129),
+                                   (8, 16, 256), (12, 16, 200)])
 def test_grid_shapes(dev, va, B, H, N):
-    """Grids with every wave count the launcher picks, and uneven XCD splits."""
+    """Grids with every wave count the launcher picks, and uneven XCD splits.
+    The last two are split-key grids of 1024 and 1344 workgroups, several per
+    compute unit."""
     wl = Workload("t", "grid", B=B, N=N, H=H, D=72, layout=LAYOUT_PACKED, layers=1, kind="iid",
                   index=60)
     li = make_layer(wl, B * 1000 + N)
