@@ -191,9 +191,10 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
 // tell the ring stage being filled from the stages being read and would put
 // a full vector-memory wait before every LDS transpose read.  The kernel
 // orders these fetches itself (vmcnt waits and a barrier before a stage is
-// read; a stage is refilled only after the barrier that ends its reads),
-// and the memory clobber keeps LDS accesses from moving across it.  Nothing
-// else in the kernel uses M0.
+// read; a stage is refilled only after the barrier that ends its reads; in
+// the split kernel a wave reads only what it fetched, after its own vmcnt
+// wait), and the memory clobber keeps LDS accesses from moving across it.
+// Nothing else in the kernel uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved: the clobber is intended
 __device__ __forceinline__ void dma16(const char* g, uint32_t off, uint32_t lds_addr) {
@@ -203,6 +204,15 @@ __device__ __forceinline__ void dma16(const char* g, uint32_t off, uint32_t lds_
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// Waits until at most n vector-memory instructions of this wave are in
+// flight (vmcnt only: expcnt 7 and lgkmcnt 15 mean no wait on those).
+// Loads, the direct-to-LDS fetches included, complete in issue order.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
 // over the 8 XCDs (id mod 8); this bijection gives each XCD a contiguous
@@ -215,9 +225,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 }
 
 // kSplit (short sequences, at most kStages key tiles, NW = 4): the waves of
-// a workgroup share one block of 32 queries, wave w reduces key tile w, and
-// the partial results are merged through LDS at the end.  This gives four
-// times the waves for grids too small to fill the chip.
+// a workgroup share one block of 32 queries, wave w fetches and reduces key
+// tile w on its own, and the partial results are merged through LDS at the
+// end.  This gives four times the waves for grids too small to fill the
+// chip.
 template <int D, int NW, bool kSplit, bool kF16>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
@@ -231,6 +242,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   // LDS ring: tile t lives in stage t % kStages and is fetched kStages-1
   // tiles ahead of the one being reduced; two workgroups share a compute unit.
   constexpr int kStages = 4;
+  // stage of stream tile s >= 0 (unsigned, so the modulo is a mask)
+  auto stage_of = [](int s) { return static_cast<int>(static_cast<unsigned>(s) % kStages); };
   static_assert(NW <= 4, "the LDS ring is sized for two workgroups of at most four waves");
   // Direct-to-LDS fetches: each wave instruction moves 64 lanes x 16 B into
   // 64 consecutive 16-byte LDS slots, 9 per K row and 10 per V row.  Slots
@@ -254,7 +267,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);
   const int col = lane & 31;   // query within the wave (MFMA column)
   const int half = lane >> 5;  // which half of the MFMA K dimension this lane feeds
 
@@ -343,8 +356,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   bool wave_active = q0 < N;
   bf16x8 qf[4];
   bf16x4 qt = {};
-  load_q(b, h, qb, qf, qt);
-  sign_q(qf, qt);
+  if constexpr (!kSplit) {  // the split kernel stages its query rows through LDS
+    load_q(b, h, qb, qf, qt);
+    sign_q(qf, qt);
+  }
   int nb = b, nh = h, nqb = qb;  // next item (the current one after the last)
   // Brings the next item's query rows of this wave into the caches, ahead
   // of load_q: one direct-to-LDS fetch of each row's
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   const uint16_t* f_vb = vbase;
   auto fetch_next = [&]() __attribute__((always_inline)) {
     if (f_s >= stream_len) return;
-    fetch_tile_at(f_kb, f_vb, f_t, f_s % kStages);
+    fetch_tile_at(f_kb, f_vb, f_t, stage_of(f_s));
     ++f_s;
     if (++f_t == ntiles && f_s < stream_len) {
       f_t = 0;
@@ -447,14 +462,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   auto wait_fetch_and_sync = [&](int tiles_in_flight, auto kLaterC) __attribute__((always_inline)) {
     constexpr int kLater = decltype(kLaterC)::value;
     asm volatile("" ::: "memory");  // the later loads stay ahead of the count
-    // vmcnt(n) only (expcnt 7, lgkmcnt 15 mean "no wait" for those counters)
-#define VITATTN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
     if (tiles_in_flight == 0) {
-      VITATTN_WAIT_VM(kLater);
+      wait_vmcnt<kLater>();
     } else {
-      VITATTN_WAIT_VM(kMinPerWave + kLater);
+      wait_vmcnt<kMinPerWave + kLater>();
     }
-#undef VITATTN_WAIT_VM
     asm volatile("s_barrier" ::: "memory");
   };
   using NoLater = std::integral_constant<int, 0>;
@@ -565,7 +577,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       // wait at the end of this step leaves it in flight, the next one not.
       if (kNext && j == ntiles - 3 && gs + 3 < stream_len) touch_q();
       // stream tile gs+1 landed before the last barrier; its V is read next step
-      if (gs + 1 < stream_len) write_ones((gs + 1) % kStages);
+      if (gs + 1 < stream_len) write_ones(stage_of(gs + 1));
     }
 
     if (wave_active) {
@@ -584,8 +596,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       }
       const float neg_m = -m_run;
       const int kb = j * kBlockN;
-      const uint16_t* kt = lds + ((gs + 1) % kStages) * kStageElems;
-      const uint16_t* vt = lds + (gs % kStages) * kStageElems + kKTile;
+      const uint16_t* kt = lds + stage_of(gs + 1) * kStageElems;
+      const uint16_t* vt = lds + stage_of(gs) * kStageElems + kKTile;
 
       float p[32];
       uint32_t w[16];
@@ -706,31 +718,87 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   f32x16 sa[2], sb[2];
 
   if constexpr (kSplit) {
-    // ---- all tiles (at most kStages) in LDS at once; wave w reduces tile w
-#pragma unroll
-    for (int t = 0; t < kStages; ++t)
-      if (t < ntiles) fetch_tile_at(kbase, vbase, t, t);
-    wait_fetch_and_sync(0, NoLater{});
+    // ---- wave w alone fetches key tile w into stage w and reduces it; no
+    // other wave touches that stage, so nothing is shared before the merge.
+    // The wave fetches the block's 32 query rows (row r at kKStride
+    // elements; rows past N repeat row N-1) into the stage's V region with
+    // its K rows, takes the query rows into registers once they land, and
+    // only then fetches its V rows over them: Q K^T runs while V is in
+    // flight.
     const int my = wave;
     if (wave_active && my < ntiles) {
-      write_ones(my);
+      const int kb0 = my * kBlockN;
+      const uint32_t stage = lds_base + 2 * my * kStageElems;
+      // fetch instructions [lo, hi) of tile my (I < kKInstr fill K slots)
+      auto fetch_own = [&](int lo, int hi) __attribute__((always_inline)) {
+        const char* gk = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb0) * a.i_st);
+        const char* gv = reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb0) * a.i_st);
+        const int last = N - 1 - kb0;
+#pragma unroll
+        for (int I = lo; I < hi; ++I) {
+          int row, cc;
+          slot_rc(I, row, cc);
+          const int r = row < last ? row : last;
+          dma16(I < kKInstr ? gk : gv, static_cast<uint32_t>((r * st32 + cc * 8) * 2),
+                stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512));
+        }
+      };
+      constexpr int kQInstr = (32 * kKSlotsRow + 63) / 64;
+      static_assert(kQInstr * 512 <= kVTile, "the query rows fit in a V tile");
+      {
+        const char* gq = reinterpret_cast<const char*>(a.q + b * a.i_sb + h * a.i_sh +
+                                                       static_cast<int64_t>(q0) * a.i_st);
+#pragma unroll
+        for (int i = 0; i < kQInstr; ++i) {
+          const int slot = i * 64 + lane;
+          int row = slot / kKSlotsRow;
+          const int c0 = slot - row * kKSlotsRow;
+          const int cc = c0 < D / 8 ? c0 : D / 8 - 1;
+          row = row < 32 ? row : 31;  // slots past the block: a copy, never read
+          row = q0 + row < N ? row : N - 1 - q0;
+          dma16(gq, static_cast<uint32_t>((row * st32 + cc * 8) * 2), stage + 2 * (kKTile + i * 512));
+        }
+      }
+      fetch_own(0, kKInstr);
+      wait_vmcnt<kKInstr>();  // the query rows landed
+      asm volatile("" ::: "memory");
+      {
+        const uint16_t* qr = lds + my * kStageElems + kKTile + col * kKStride;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * half);
+        if constexpr (D == 72) qt = *reinterpret_cast<const bf16x4*>(qr + 64 + 4 * half);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the V rows land on them
+      sign_q(qf, qt);
+      fetch_own(kKInstr, kInstr);
+      wait_vmcnt<kVInstr>();  // the K rows landed
+      asm volatile("" ::: "memory");
       qk_plain(lds + my * kStageElems, sa);
       mx = rowmax(sa);
+      asm volatile("" ::"v"(mx));  // the row max is taken before the wait below
+      wait_vmcnt<0>();             // the V rows landed
+      asm volatile("" ::: "memory");
+      write_ones(my);
       if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{});
       else step(my, my, sa, sb, False{}, False{});
     }
     // ---- merge the partial results of the waves (each: running max m,
-    // accumulator, and for D = 64 the partial row sum) through LDS, laid out
-    // [wave][group of 4 registers][lane][4] so every access is 1 KB contiguous
+    // accumulator, and for D = 64 the partial row sum) through LDS.  Wave w
+    // writes its part into its own stage, which no other wave has touched,
+    // laid out [group of 4 registers][lane][4] so every access is 1 KB
+    // contiguous; one barrier then orders the writes before the reads.
     if (!wave_active) return;  // the whole workgroup shares this predicate
     constexpr int kGroups = kOutTiles * 4 + 1;         // acc groups + (m, l)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage reads done
+    static_assert(kGroups * 64 * 4 * 4 <= kStageElems * 2, "the merge slots fit in a stage");
     float* mb = reinterpret_cast<float*>(lds);
-    auto slot = [&](int w, int g) { return mb + ((w * kGroups + g) * 64 + lane) * 4; };
+    auto slot = [&](int w, int g) { return mb + w * (kStageElems / 2) + (g * 64 + lane) * 4; };
 #pragma unroll
     for (int mt = 0; mt < kOutTiles; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        // groups past output row D are never read (for D = 72, tile 2's
+        // group 1 holds the row sum)
+        if (32 * mt + 8 * g > D) continue;
         const f32x4 v = {acc[mt][4 * g], acc[mt][4 * g + 1], acc[mt][4 * g + 2], acc[mt][4 * g + 3]};
         *reinterpret_cast<f32x4*>(slot(wave, mt * 4 + g)) = v;
       }
@@ -747,9 +815,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
       mw[w] = ml[0];
       if constexpr (kOnesRow) {
         // the row sum is output row D: tile 2, register 4, lanes with half 0
-        lw[w] = mb[((w * kGroups + 9) * 64 + col) * 4];
+        lw[w] = mb[w * (kStageElems / 2) + (9 * 64 + col) * 4];
       } else {
-        lw[w] = ml[1] + mb[((w * kGroups + kOutTiles * 4) * 64 + (lane ^ 32)) * 4 + 1];
+        lw[w] = ml[1] + mb[w * (kStageElems / 2) + (kOutTiles * 4 * 64 + (lane ^ 32)) * 4 + 1];
       }
     }
     const float mstar = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
@@ -809,7 +877,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     // S_0 of the item and its row max in registers (stream tile g0 landed
     // before the last barrier)
     if (wave_active) {
-      qk_plain(lds + (g0 % kStages) * kStageElems, sa);
+      qk_plain(lds + stage_of(g0) * kStageElems, sa);
       mx = rowmax(sa);
     }
     int j = 0;
@@ -833,7 +901,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
     {
       constexpr int kOS = 72;  // row stride of the staged tile (elements)
       static_assert(NW * 32 * kOS <= kStageElems, "staged output tile must fit in a stage");
-      uint16_t* ob = lds + ((g0 + ntiles - 1) % kStages) * kStageElems + wave * 32 * kOS;
+      uint16_t* ob = lds + stage_of(g0 + ntiles - 1) * kStageElems + wave * 32 * kOS;
       if (wave_active) {
         float l;
         if constexpr (kOnesRow) {
