@@ -161,14 +161,30 @@ def _roofline(wl, launch_s):
             "frac": ach / PEAK_HBM_GBPS, "traffic": traffic}
 
 
-def _time_steps(va, wl, ins, outs, steps, warmup, stream):
+def _time_steps(va, wl, ins, outs, steps, warmup, stream, checked=False):
     """Warmup, then exactly `steps` timed steps bracketed by two events on the
-    stream the kernels are launched on.  Returns (total ms, wall seconds)."""
+    stream the kernels are launched on.  Returns (total ms, wall seconds).
+
+    A step is one C-ABI call (vitattn_fwd) per layer.  The calls' arguments
+    are checked and marshalled once, before the timed region (`fwd_args`);
+    with `checked`, every call goes through the checking torch wrapper
+    `fwd` instead, whose host time per call can exceed a short kernel's."""
     import torch
 
-    def step():
-        for ts, o in zip(ins, outs):
-            va.fwd(ts[0], ts[1], ts[2], out=o, scale=wl.scale, stream=stream)
+    if checked:
+        def step():
+            for ts, o in zip(ins, outs):
+                va.fwd(ts[0], ts[1], ts[2], out=o, scale=wl.scale, stream=stream)
+    else:
+        calls = [va.fwd_args(ts[0], ts[1], ts[2], out=o, scale=wl.scale, stream=stream)
+                 for ts, o in zip(ins, outs)]
+        fwd_raw = va.fwd_raw
+
+        def step():
+            for c in calls:
+                rc = fwd_raw(*c)
+                if rc:
+                    raise va.VitAttnError(rc, va.strerror(rc))
 
     for _ in range(warmup):
         step()
@@ -512,6 +528,13 @@ def main():
                       "tflops": wl.flops_per_layer * wl.layers / (p_ms * 1e-3) / 1e12,
                       "timing": "the step's layer calls recorded once into a HIP graph "
                                 "(vitattn_plan_create), one graph launch per step"}
+    # the same step through the checking torch wrapper, per call
+    c_ms, c_wall = _time_steps(va, wl, ins, outs, args.steps, args.warmup, stream, checked=True)
+    result["checked_wrapper"] = {
+        "ms_per_step": c_ms / args.steps, "us_per_layer": c_ms * 1e3 / args.steps / wl.layers,
+        "host_us_per_call": c_wall * 1e6 / args.steps / wl.layers,
+        "timing": "vit_self_attention_amd.fwd(tensors) per layer call: the arguments are "
+                  "checked on every call"}
 
     if not args.no_cpu_baseline:
         cpu, refs = _cpu_baseline(wl, host, args.cpu_seconds)

@@ -235,6 +235,30 @@ def test_deterministic(dev, va):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_prepared_call_matches_fwd(dev, va):
+    """fwd_args + fwd_raw (checked once, called many times) gives fwd's bits,
+    in both layouts."""
+    import torch
+    wl = WORKLOADS["c3"]
+    li = make_layer(wl, 5)
+    qkv = to_device(li.packed(), dev)
+    ref = va.fwd(qkv, scale=wl.scale)
+    out = torch.empty_like(ref)
+    args = va.fwd_args(qkv, out=out, scale=wl.scale)
+    for _ in range(3):
+        assert va.fwd_raw(*args) == va.OK
+    torch.cuda.synchronize(dev)
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
+    q, k, v = (to_device(a, dev) for a in li.in_layout(LAYOUT_SEPARATE))
+    ref = va.fwd(q, k, v, scale=wl.scale)
+    out = torch.empty_like(ref)
+    assert va.fwd_raw(*va.fwd_args(q, k, v, out=out, scale=wl.scale)) == va.OK
+    torch.cuda.synchronize(dev)
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
+    with pytest.raises(ValueError):
+        va.fwd_args(qkv, out=None)
+
+
 @pytest.mark.parametrize("N", [1, 33, 101, 257])
 def test_no_writes_outside_out(dev, va, N):
     """Guard regions before and after `out` keep their pattern (ragged tails

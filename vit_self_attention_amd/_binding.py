@@ -130,6 +130,26 @@ def _layout_of(q_or_qkv, k, v, out):
     return B, H, N, D, layout, out_shape
 
 
+def fwd_args(q_or_qkv, k=None, v=None, *, out, scale: float | None = None, stream=None) -> tuple:
+    """Checks a forward call once, as `fwd` does, and returns its C-ABI
+    arguments (device addresses, sizes, scale, layout, stream handle) for
+    repeated `fwd_raw(*args)` calls on the same tensors: loops that launch a
+    fixed set of calls skip the per-call checks.  The tensors must stay
+    alive, unmoved, while the arguments are used."""
+    import torch
+
+    if out is None:
+        raise ValueError("fwd_args needs a preallocated out")
+    B, H, N, D, layout, _ = _layout_of(q_or_qkv, k, v, out)
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if stream is None:
+        stream = torch.cuda.current_stream(q_or_qkv.device)
+    return (q_or_qkv.data_ptr(), k.data_ptr() if k is not None else None,
+            v.data_ptr() if v is not None else None, out.data_ptr(), B, H, N, D, float(scale),
+            layout, stream.cuda_stream)
+
+
 def fwd(q_or_qkv, k=None, v=None, *, out=None, scale: float | None = None, stream=None):
     """O = softmax(scale * Q K^T) V per (image, head), on the GPU.
 
