@@ -31,6 +31,10 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 VALU forms stay off: hipcc must not emit them for this code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the attention kernel's first ten (scalar) arguments, 14 dwords, are
+    # preloaded into SGPRs at wave launch instead of read from memory; kernels
+    # that take a struct are unaffected
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
 ]
 
 

@@ -71,6 +71,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <bool kF16>
 constexpr float lazy_bound() { return kF16 ? 8.0f : 64.0f; }
 
+// What the kernel works with; it arrives as scalar kernel arguments (see
+// fwd_kernel) and the strides are derived from the layout in the kernel.
 struct KernelArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -230,7 +232,37 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 // end.  This gives four times the waves for grids too small to fill the
 // chip.
 template <int D, int NW, bool kSplit, bool kF16>
-__global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int H, int N_, int i_st,
+                                                      float cs, const uint16_t* q, const uint16_t* k,
+                                                      const uint16_t* v, uint16_t* o, int items) {
+  // The arguments are scalars, all but `items` (14 dwords) preloaded into
+  // SGPRs at wave launch instead of read from the argument buffer; the
+  // looping kernel alone reads `items`.  cs is the softmax factor c, negated
+  // when the scale is negative (Q is then negated instead).  The strides
+  // follow from the layout: separate [B,H,N,D] rows are D apart, packed
+  // [B,N,3,H,D] rows 3*H*D, and the output is [B,H,N,D] or [B,N,H,D].
+  KernelArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.i_st = i_st;
+  a.H = H;
+  a.N = N_;
+  a.qblocks = qblocks;
+  a.items = items;
+  a.grid = grid;
+  a.c = __builtin_fabsf(cs);
+  a.qsign = cs < 0.f ? 0x80008000u : 0u;
+  {
+    const bool sep = i_st == D;
+    const int64_t nd = static_cast<int64_t>(N_) * D;
+    a.i_sh = sep ? nd : D;
+    a.i_sb = sep ? H * nd : static_cast<int64_t>(N_) * i_st;
+    a.o_sb = H * nd;
+    a.o_sh = sep ? nd : D;
+    a.o_st = sep ? D : H * D;
+  }
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
   constexpr int kOutTiles = kOnesRow ? 3 : 2;
   // V row: D values (+ [1,0,..,0] for D = 72) in a 160-byte row; with the key
@@ -287,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
   int it0 = 0, lo = 0, gx = 1, ky = 1, lx = 0;
   bool single = true;
   int nitems = 1;
-  if (a.grid >= a.items) {
+  if (kSplit || a.grid >= a.items) {  // the split kernel never loops
     it0 = xcd_remap(blockIdx.x, a.grid);
   } else {
     single = false;
@@ -946,7 +978,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(KernelArgs a) {
 
 template <int D, int NW, bool kSplit, bool kF16>
 int launch(const KernelArgs& ka, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit, kF16>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit, kF16>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka.grid,
+                     ka.qblocks, ka.H, ka.N, ka.i_st, ka.qsign ? -ka.c : ka.c, ka.q, ka.k, ka.v, ka.o, ka.items);
   return hipGetLastError() == hipSuccess ? VITATTN_OK : VITATTN_ERR_LAUNCH;
 }
 
@@ -1017,6 +1050,16 @@ int launch_fwd(const FwdArgs& f, void* stream) {
       f.k_st != f.q_st || f.v_st != f.q_st || 64 * f.q_st >= (int64_t(1) << 30) ||
       64 * f.o_st >= (int64_t(1) << 30))
     return VITATTN_ERR_LAUNCH;
+  {
+    // the kernel derives every stride from the layout (contiguous tensors)
+    const int64_t nd = static_cast<int64_t>(f.N) * f.D, hd = static_cast<int64_t>(f.H) * f.D;
+    const bool sep = f.q_st == f.D;
+    const bool ok = sep ? (f.q_sh == nd && f.q_sb == f.H * nd && f.o_st == f.D && f.o_sh == nd &&
+                           f.o_sb == f.H * nd)
+                        : (f.q_st == 3 * hd && f.q_sh == f.D && f.q_sb == f.N * 3 * hd &&
+                           f.o_st == hd && f.o_sh == f.D && f.o_sb == f.N * hd);
+    if (!ok) return VITATTN_ERR_LAUNCH;
+  }
   ka.i_sb = f.q_sb;
   ka.i_sh = f.q_sh;
   ka.i_st = static_cast<int>(f.q_st);
