@@ -596,10 +596,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // while the matrix core works.
   // j is the tile's index in its item, gs its index in the tile stream
   // (gs = j for the split kernel, whose stage of tile j is stage j).
-  auto step = [&](int j, int gs, f32x16* cur, f32x16* nxt, auto kNextC, auto kRaggedC)
-                  __attribute__((always_inline)) {
+  auto step = [&](int j, int gs, f32x16* cur, f32x16* nxt, auto kNextC, auto kRaggedC,
+                  auto kHalfC) __attribute__((always_inline)) {
     constexpr bool kNext = decltype(kNextC)::value;
     constexpr bool kRagged = decltype(kRaggedC)::value;
+    // kHalf (the item's last step only): the tile holds at most 32 keys, so
+    // only its first 32-key block is weighted and multiplied into P V; its
+    // keys 32..63 would all get zero weight.  (Q K^T of the tile ran a step
+    // earlier over both blocks.)
+    constexpr bool kThisHalf = decltype(kHalfC)::value;
+    static_assert(!(kThisHalf && kNext), "only the last step reduces a half tile");
     if constexpr (!kSplit) {
       // stage (gs-1) % kStages held stream tile gs-1, whose reads all ended
       // before the last barrier; it is refilled with stream tile gs + kStages - 1
@@ -677,12 +683,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 24; ++e) do_exp(e);
+        for (int e = 0; e < (kThisHalf ? 16 : 24); ++e) do_exp(e);
       }
 
       // phases 2 and 3: P V of tile j; the remaining weights ride along the
       // first half, the row max of tile j+1 the second half
-      constexpr int kPv = 4 * kOutTiles, kHalfPv = 2 * kOutTiles;
+      // (a half tile: keys 0..31 only, all weighted in phase 1)
+      constexpr int kPv = (kThisHalf ? 2 : 4) * kOutTiles, kHalfPv = 2 * kOutTiles;
       bf16x8 vo[kPv];
       vo[0] = v_read(vt, 0);
       vo[1] = v_read(vt, 1);
@@ -694,8 +701,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
         const int t = i / kOutTiles, mt = i % kOutTiles;
         acc[mt] = mma_32x32x16<kF16>(vo[i], pb(t), acc[mt]);
         if (i < kHalfPv) {
+          if constexpr (!kThisHalf) {
 #pragma unroll
-          for (int e = 24 + 8 * i / kHalfPv; e < 24 + 8 * (i + 1) / kHalfPv; ++e) do_exp(e);
+            for (int e = 24 + 8 * i / kHalfPv; e < 24 + 8 * (i + 1) / kHalfPv; ++e) do_exp(e);
+          }
         } else if constexpr (kNext) {
           const int ii = i - kHalfPv;
 #pragma unroll
@@ -747,6 +756,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
   const bool ragged = N % kBlockN != 0;
+  // the last key tile holds at most 32 keys
+  const bool half_tail = ragged && N % kBlockN <= 32;
   f32x16 sa[2], sb[2];
 
   if constexpr (kSplit) {
@@ -811,8 +822,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       wait_vmcnt<0>();             // the V rows landed
       asm volatile("" ::: "memory");
       write_ones(my);
-      if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{});
-      else step(my, my, sa, sb, False{}, False{});
+      if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{}, False{});
+      else step(my, my, sa, sb, False{}, False{}, False{});
     }
     // ---- merge the partial results of the waves (each: running max m,
     // accumulator, and for D = 64 the partial row sum) through LDS.  Wave w
@@ -914,16 +925,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     }
     int j = 0;
     for (; j + 2 < ntiles; j += 2) {
-      step(j, g0 + j, sa, sb, True{}, False{});
-      step(j + 1, g0 + j + 1, sb, sa, True{}, False{});
+      step(j, g0 + j, sa, sb, True{}, False{}, False{});
+      step(j + 1, g0 + j + 1, sb, sa, True{}, False{}, False{});
     }
     if (j + 1 < ntiles) {
-      step(j, g0 + j, sa, sb, True{}, False{});
-      if (ragged) step(j + 1, g0 + j + 1, sb, sa, False{}, True{});
-      else step(j + 1, g0 + j + 1, sb, sa, False{}, False{});
+      step(j, g0 + j, sa, sb, True{}, False{}, False{});
+      if (half_tail) step(j + 1, g0 + j + 1, sb, sa, False{}, True{}, True{});
+      else if (ragged) step(j + 1, g0 + j + 1, sb, sa, False{}, True{}, False{});
+      else step(j + 1, g0 + j + 1, sb, sa, False{}, False{}, False{});
     } else {
-      if (ragged) step(j, g0 + j, sa, sb, False{}, True{});
-      else step(j, g0 + j, sa, sb, False{}, False{});
+      // (an odd tile count or a single tile: this tile's Q K^T ran in the
+      // loop or before it)
+      if (half_tail) step(j, g0 + j, sa, sb, False{}, True{}, True{});
+      else if (ragged) step(j, g0 + j, sa, sb, False{}, True{}, False{});
+      else step(j, g0 + j, sa, sb, False{}, False{}, False{});
     }
 
     // ---- epilogue: O = acc / l in bf16, rows < N only.  The tile goes
