@@ -52,7 +52,10 @@ def test_workload_parity_all_layers(dev, va, key):
 
 # ---------------------------------------------------------------- ragged sizes
 
-RAGGED_N = [1, 2, 3, 31, 32, 33, 63, 64, 65, 101, 127, 128, 129, 197, 255, 256, 257, 300]
+# includes last key tiles of 1, 32 and 33 keys after an odd and an even
+# number of full tiles (288 = 4*64 + 32, 321 = 5*64 + 1, 353 = 5*64 + 33)
+RAGGED_N = [1, 2, 3, 31, 32, 33, 63, 64, 65, 101, 127, 128, 129, 197, 255, 256, 257, 288, 300,
+            321, 353]
 
 
 @pytest.mark.parametrize("D", [64, 72])
