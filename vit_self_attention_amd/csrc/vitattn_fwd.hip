@@ -851,10 +851,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // wave w finalizes register group w of every output tile
+    // (single-float reads: the loads are independent and all in flight at once)
     float mw[4], lw[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const f32x4 ml = *reinterpret_cast<const f32x4*>(slot(w, kOutTiles * 4));
+      const float* ml = slot(w, kOutTiles * 4);
       mw[w] = ml[0];
       if constexpr (kOnesRow) {
         // the row sum is output row D: tile 2, register 4, lanes with half 0
