@@ -146,6 +146,11 @@ def test_python_wrapper_rejects_cpu_tensors(va):
     x = torch.zeros(1, 4, 3, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         va.fwd(x)
+    # the prepared-call helper runs the same checks, and needs an output
+    with pytest.raises(ValueError):
+        va.fwd_args(x, out=None)
+    with pytest.raises(TypeError):
+        va.fwd_args(x, out=torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16))
 
 
 # ---- plans (recorded call sequences).  Every case below fails a host-side
