@@ -92,7 +92,7 @@ def test_linear_kernels_m0_and_registers(linear_asm):
     """The linear kernels use the same direct-to-LDS fetch sequence, spill
     nothing and fit two waves per SIMD."""
     ks = _kernels(linear_asm, "linear_kernel")
-    assert len(ks) == 6, list(ks)  # three tile shapes x {bf16, fp16}
+    assert len(ks) == 8, list(ks)  # four tile shapes x {bf16, fp16}
     for name, (body, meta) in ks.items():
         for i, ln in enumerate(body):
             if "m0" in ln:

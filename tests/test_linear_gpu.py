@@ -131,6 +131,19 @@ def test_ragged_shapes(dev, va, M, K, Nout):
     _check(_host(y), x, w, b, r, "bf16", what=f"M={M} K={K} Nout={Nout}")
 
 
+# one shape per tile configuration the launcher picks, each with ragged M and
+# Nout: 256 x 256, 128 x 128, 64 x 128 and 64 x 64 tiles
+@pytest.mark.parametrize("M,K,Nout", [(4100, 64, 4104), (2100, 96, 2056), (1000, 64, 2056),
+                                      (300, 96, 264)])
+def test_every_tile_config(dev, va, M, K, Nout):
+    import torch
+    x, w, b, r = _inputs(30 + M, M, K, Nout, "bf16", residual=True)
+    td = [_dev(t, "bf16", dev) for t in (x, w, b, r)]
+    y = va.linear(td[0], td[1], td[2], residual=td[3])
+    torch.cuda.synchronize(dev)
+    _check(_host(y), x, w, b, r, "bf16", what=f"M={M} K={K} Nout={Nout}")
+
+
 def test_no_bias_no_residual_and_determinism(dev, va):
     import torch
     M, K, Nout = 1000, 256, 512

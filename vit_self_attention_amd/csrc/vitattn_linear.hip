@@ -267,14 +267,15 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   // col.  Each 32-token slab i of the wave's tile goes through the wave's
   // own LDS region as fp32 (the ring is free once every wave has left the
   // loop), and comes back as rows: lane l then holds 8 consecutive features
-  // of one token, adds bias and residual and writes 16 bytes, eight lanes
-  // covering one 128-byte row segment.
+  // of one token, adds bias and residual and writes 16 bytes, TN/8 lanes
+  // covering one row segment of the tile (128 bytes for TN = 64).
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   constexpr int kSlabStride = TN + 4;  // floats per staged row (272 bytes for TN = 64)
   static_assert(NW * 32 * kSlabStride * 4 <= kStagesL * kStageElems * 2, "staging fits in the ring");
-  static_assert(TN == 64, "eight lanes of 8 features per staged row");
+  constexpr int kLanesRow = TN / 8, kRowsRead = 64 / kLanesRow;  // read-back: lanes per row, rows per pass
+  static_assert(TN % 8 == 0 && 32 % kRowsRead == 0, "whole rows per read-back pass");
   float* slab = reinterpret_cast<float*>(lds) + wave * 32 * kSlabStride;
-  const int rrow = lane >> 3, rch = lane & 7;       // read-back: row within 8, 8-feature chunk
+  const int rrow = lane / kLanesRow, rch = lane % kLanesRow;  // row within the pass, 8-feature chunk
   const int n = n0 + wn * TN + 8 * rch;
   float bsum[8];
 #pragma unroll
@@ -298,8 +299,8 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
         *reinterpret_cast<float4*>(slab + col * kSlabStride + 32 * j + 8 * g + 4 * half) = v;
       }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 8 * q + rrow;
+    for (int q = 0; q < 32 / kRowsRead; ++q) {
+      const int row = kRowsRead * q + rrow;
       const float4 lo = *reinterpret_cast<const float4*>(slab + row * kSlabStride + 8 * rch);
       const float4 hi = *reinterpret_cast<const float4*>(slab + row * kSlabStride + 8 * rch + 4);
       const int m = m0 + wm * TM + 32 * i + row;
@@ -343,12 +344,17 @@ template <bool kF16>
 int launch_linear_typed(const LinearArgs& la, hipStream_t s) {
   // the largest tiles that still give a workgroup per compute unit (256 on
   // MI355X): 256 x 256 (eight waves of 128 x 64), 128 x 128 (four waves of
-  // 64 x 64), else 64 x 128 (four waves of 32 x 64)
+  // 64 x 64); below that, 64 x 64 tiles (four waves of 32 x 32) while they
+  // number at most 448, else 64 x 128 (four waves of 32 x 64).  (On the
+  // 224 px projections, M = 512: 64 x 64 tiles take the output projection
+  // from 10.0 to 8.4 us and the qkv projection from 10.2 to 9.7 us; past
+  // about 1.75 tiles per compute unit the 64 x 128 tiles are faster.)
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((la.M + bm - 1) / bm) * ((la.Nout + bn - 1) / bn);
   };
   if (tiles(256, 256) >= 256) return launch_linear_cfg<2, 4, 128, 64, kF16>(la, s);
   if (tiles(128, 128) >= 256) return launch_linear_cfg<2, 2, 64, 64, kF16>(la, s);
+  if (tiles(64, 64) <= 448) return launch_linear_cfg<2, 2, 32, 32, kF16>(la, s);
   return launch_linear_cfg<2, 2, 32, 64, kF16>(la, s);
 }
 
