@@ -550,6 +550,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
         s[blk] = mma_32x32x8<kF16>(k_read_tail(kt, blk), qt, s[blk]);
     }
   };
+  // S^T of one 32-key block (rows 32*blk .. 32*blk+31 of the tile)
+  auto qk_block = [&](const uint16_t* kt, f32x16* s, int blk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) s[blk] = mma_32x32x16<kF16>(k_read(kt, 2 * st + blk), qf[st], s[blk]);
+    if constexpr (D == 72) s[blk] = mma_32x32x8<kF16>(k_read_tail(kt, blk), qt, s[blk]);
+  };
   // V^T operand of P V step idx = t*kOutTiles + mt (keys 16t.., output rows 32mt..)
   auto v_read = [&](const uint16_t* vt, int idx) {
     const int t = idx / kOutTiles, mt = idx % kOutTiles;
@@ -697,6 +705,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kPv; ++i) {
+        if constexpr (kSplit && !kThisHalf) {
+          // the split kernel enters with V rows 0..31 landed; rows 32..63
+          // (keys of steps t = 2, 3) are waited for before their first read
+          if (i + 2 == kHalfPv) {
+            wait_vmcnt<0>();
+            asm volatile("" ::: "memory");
+            if (half == 1) write_ones(gs);
+          }
+        }
         if (i + 2 < kPv) vo[i + 2] = v_read(vt, i + 2);
         const int t = i / kOutTiles, mt = i % kOutTiles;
         acc[mt] = mma_32x32x16<kF16>(vo[i], pb(t), acc[mt]);
@@ -814,14 +831,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the V rows land on them
       sign_q(qf, qt);
       fetch_own(kKInstr, kInstr);
+      // K rows 0..35 (the first five fetches) carry key block 0, the rest
+      // block 1; V rows 0..31 (the first five) keys 0..31 of P V
+      constexpr int kHalfFetch = 5;
+      static_assert(kHalfFetch * 64 >= 32 * kKSlotsRow && kHalfFetch * 64 == 32 * kVSlotsRow,
+                    "five fetches cover 32 rows of K and exactly 32 of V");
+      wait_vmcnt<kVInstr + kKInstr - kHalfFetch>();
+      asm volatile("" ::: "memory");
+      qk_block(lds + my * kStageElems, sa, 0);
       wait_vmcnt<kVInstr>();  // the K rows landed
       asm volatile("" ::: "memory");
-      qk_plain(lds + my * kStageElems, sa);
+      qk_block(lds + my * kStageElems, sa, 1);
       mx = rowmax(sa);
       asm volatile("" ::"v"(mx));  // the row max is taken before the wait below
-      wait_vmcnt<0>();             // the V rows landed
+      wait_vmcnt<kVInstr - kHalfFetch>();  // V rows 0..31 landed
       asm volatile("" ::: "memory");
-      write_ones(my);
+      if (half == 0) write_ones(my);  // rows 0..31 (lane = row); rows 32..63 in the step
       if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{}, False{});
       else step(my, my, sa, sb, False{}, False{}, False{});
     }
