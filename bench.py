@@ -166,7 +166,8 @@ def _time_steps(va, wl, ins, outs, steps, warmup, stream, checked=False):
     stream the kernels are launched on.  Returns (total ms, wall seconds).
 
     A step is one C-ABI call (vitattn_fwd) per layer.  The calls' arguments
-    are checked and marshalled once, before the timed region (`fwd_args`);
+    are checked and marshalled once, before the timed region (`fwd_args`),
+    and the loop calls the C function itself (`fwd_c`);
     with `checked`, every call goes through the checking torch wrapper
     `fwd` instead, whose host time per call can exceed a short kernel's."""
     import torch
@@ -178,13 +179,14 @@ def _time_steps(va, wl, ins, outs, steps, warmup, stream, checked=False):
     else:
         calls = [va.fwd_args(ts[0], ts[1], ts[2], out=o, scale=wl.scale, stream=stream)
                  for ts, o in zip(ins, outs)]
-        fwd_raw = va.fwd_raw
+        fwd_c = va.fwd_c
 
         def step():
+            bad = 0
             for c in calls:
-                rc = fwd_raw(*c)
-                if rc:
-                    raise va.VitAttnError(rc, va.strerror(rc))
+                bad |= fwd_c(*c)
+            if bad:
+                raise RuntimeError(f"vitattn_fwd returned an error in the timed loop ({bad})")
 
     for _ in range(warmup):
         step()

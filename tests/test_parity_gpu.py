@@ -250,6 +250,7 @@ def test_prepared_call_matches_fwd(dev, va):
     args = va.fwd_args(qkv, out=out, scale=wl.scale)
     for _ in range(3):
         assert va.fwd_raw(*args) == va.OK
+        assert va.fwd_c(*args) == va.OK
     torch.cuda.synchronize(dev)
     assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
     q, k, v = (to_device(a, dev) for a in li.in_layout(LAYOUT_SEPARATE))

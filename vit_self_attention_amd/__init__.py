@@ -15,10 +15,10 @@ from ._binding import (ERR_BAD_LAYOUT, ERR_BAD_SCALE, ERR_BAD_SIZE, ERR_GRAPH, E
                        ERR_MISALIGNED, ERR_NULL_POINTER, ERR_OVERLAP, ERR_TOO_LARGE,
                        ERR_UNSUPPORTED_D, ERR_UNSUPPORTED_SHAPE, EXPORTED, DTYPE_FP16,
                        LAYOUT_PACKED, LAYOUT_SEPARATE, LIBRARY, OK, Plan, VitAttnError, fwd,
-                       fwd_args, fwd_raw, linear, linear_raw, plan_create_raw, plan_destroy_raw,
+                       fwd_args, fwd_c, fwd_raw, linear, linear_raw, plan_create_raw, plan_destroy_raw,
                        plan_launch_raw, strerror, version)
 
-__all__ = ["fwd", "fwd_args", "fwd_raw", "linear", "linear_raw", "Plan", "plan_create_raw", "plan_launch_raw", "plan_destroy_raw",
+__all__ = ["fwd", "fwd_args", "fwd_c", "fwd_raw", "linear", "linear_raw", "Plan", "plan_create_raw", "plan_launch_raw", "plan_destroy_raw",
            "strerror", "version", "VitAttnError", "LAYOUT_PACKED", "LAYOUT_SEPARATE", "DTYPE_FP16",
            "LIBRARY",
            "EXPORTED"]

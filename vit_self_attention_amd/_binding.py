@@ -87,6 +87,11 @@ def fwd_raw(qkv_or_q: int, k: int | None, v: int | None, out: int, B: int, H: in
                            int(N), int(D), float(scale), int(layout), stream or None)
 
 
+# vitattn_fwd itself as a ctypes function, for the argument tuples fwd_args
+# returns: fwd_c(*args) -> status, with no Python-level conversion
+fwd_c = lib.vitattn_fwd
+
+
 def _layout_of(q_or_qkv, k, v, out):
     """Checks torch tensors as the C ABI expects them; returns
     (B, H, N, D, layout, out_shape), the layout carrying the fp16 flag for
@@ -133,8 +138,8 @@ def _layout_of(q_or_qkv, k, v, out):
 def fwd_args(q_or_qkv, k=None, v=None, *, out, scale: float | None = None, stream=None) -> tuple:
     """Checks a forward call once, as `fwd` does, and returns its C-ABI
     arguments (device addresses, sizes, scale, layout, stream handle) for
-    repeated `fwd_raw(*args)` calls on the same tensors: loops that launch a
-    fixed set of calls skip the per-call checks.  The tensors must stay
+    repeated `fwd_raw(*args)` or `fwd_c(*args)` calls on the same tensors:
+    loops that launch a fixed set of calls skip the per-call checks.  The tensors must stay
     alive, unmoved, while the arguments are used."""
     import torch
 
