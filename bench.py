@@ -520,6 +520,10 @@ def main():
         "hbm_gbps": wl.bytes_per_layer * wl.layers / (ms_per_step * 1e-3) / 1e9,
         "roofline": roof,
         "wall_s_timed": wall,
+        "host_us_per_call": wall * 1e6 / args.steps / wl.layers,
+        "call": ("vitattn_fwd through the vectorcall module _vitattn_ext"
+                 if type(va.fwd_c).__name__ == "builtin_function_or_method"
+                 else "vitattn_fwd through ctypes"),
     }
 
     # the same step recorded once as a plan (one HIP graph of all layer calls)

@@ -141,6 +141,55 @@ def test_empty_problem_is_a_noop(va, bhn):
     assert _call(va, q=0, out=0, B=B, H=H, N=N, D=80) == va._binding.ERR_UNSUPPORTED_D
 
 
+def test_vectorcall_module_matches_ctypes_statuses(va):
+    """The vectorcall module built beside the library is the binding's
+    fwd_c, and returns what the ctypes function returns for every argument
+    check (none of these calls reaches the device)."""
+    from vit_self_attention_amd import _vitattn_ext
+
+    assert va.fwd_c is _vitattn_ext.vitattn_fwd
+    kk, vv = A + 2 ** 30, A + 2 ** 31
+    cases = [
+        (A, None, None, OUT, 2, 3, 197, 65, 0.125, 1, None),           # unsupported D
+        (A, None, None, OUT, -1, 3, 197, 64, 0.125, 1, None),          # negative B
+        (A, None, None, OUT, 2, 3, 197, 64, math.nan, 1, None),        # NaN scale
+        (None, None, None, OUT, 2, 3, 197, 64, 0.125, 1, None),        # NULL input
+        (A, None, None, OUT, 2, 3, 197, 64, 0.125, 2, None),           # bad layout
+        (A + 2, None, None, OUT, 2, 3, 197, 64, 0.125, 1, None),       # misaligned
+        (A, kk, vv, vv + 1024, 2, 3, 197, 64, 0.125, 0, None),         # out overlaps v
+        (A, None, None, OUT, 2 ** 30, 2 ** 10, 2 ** 10, 64, 0.125, 1, None),  # too large
+        (A, None, None, OUT, 0, 3, 7, 64, 0.125, 1, None),             # empty: no-op
+        (0, None, None, 0, 2, 3, 0, 64, 0.125, 1, 0),                  # empty, NULL stream 0
+    ]
+    for args in cases:
+        want = va._binding.lib.vitattn_fwd(*[x if x else None for x in args[:4]], *args[4:10],
+                                           args[10] or None)
+        assert _vitattn_ext.vitattn_fwd(*args) == want, args
+    assert _vitattn_ext.vitattn_fwd(*cases[0]) == va._binding.ERR_UNSUPPORTED_D
+
+
+def test_vectorcall_module_rejects_bad_python_arguments(va):
+    from vit_self_attention_amd import _vitattn_ext as ext
+
+    good = (A, None, None, OUT, 2, 3, 197, 65, 0.125, 1, None)
+    with pytest.raises(TypeError):
+        ext.vitattn_fwd(*good[:10])
+    with pytest.raises(TypeError):
+        ext.vitattn_fwd(*good, None)
+    with pytest.raises(TypeError):
+        ext.vitattn_fwd("0x10", *good[1:])
+    with pytest.raises(TypeError):
+        ext.vitattn_fwd(*good[:4], 2.0, *good[5:])
+    with pytest.raises(TypeError):
+        ext.vitattn_fwd(*good[:8], "0.125", *good[9:])
+    with pytest.raises(OverflowError):
+        ext.vitattn_fwd(*good[:6], 2 ** 31, *good[7:])
+    with pytest.raises(OverflowError):
+        ext.vitattn_fwd(-1, *good[1:])
+    # a float scale may arrive as an int
+    assert ext.vitattn_fwd(*good[:8], 1, *good[9:]) == va._binding.ERR_UNSUPPORTED_D
+
+
 def test_python_wrapper_rejects_cpu_tensors(va):
     import torch
     x = torch.zeros(1, 4, 3, 2, 64, dtype=torch.bfloat16)

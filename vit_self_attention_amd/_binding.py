@@ -87,9 +87,15 @@ def fwd_raw(qkv_or_q: int, k: int | None, v: int | None, out: int, B: int, H: in
                            int(N), int(D), float(scale), int(layout), stream or None)
 
 
-# vitattn_fwd itself as a ctypes function, for the argument tuples fwd_args
-# returns: fwd_c(*args) -> status, with no Python-level conversion
-fwd_c = lib.vitattn_fwd
+# vitattn_fwd itself, for the argument tuples fwd_args returns:
+# fwd_c(*args) -> status, with no Python-level conversion.  The vectorcall
+# module built beside the library converts the eleven arguments in a few
+# hundred nanoseconds; the ctypes function (about 2 us) serves when that
+# module has not been built.
+try:
+    from ._vitattn_ext import vitattn_fwd as fwd_c
+except ImportError:
+    fwd_c = lib.vitattn_fwd
 
 
 def _layout_of(q_or_qkv, k, v, out):

@@ -58,9 +58,38 @@ def _hipcc(sources, library, verbose):
     return library
 
 
+# Python module that calls vitattn_fwd with vectorcall arguments (host C,
+# linked against libvitattn.so next to it)
+EXT_SOURCE = os.path.join(CSRC, "vitattn_pyext.c")
+
+
+def _ext_path() -> str:
+    import sysconfig
+
+    return os.path.join(PKG, "_vitattn_ext" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def _build_ext(verbose):
+    import sysconfig
+
+    ext = _ext_path()
+    tmp = ext + ".tmp"
+    cmd = [os.environ.get("CC", "gcc"), "-O2", "-shared", "-fPIC", "-Wall", "-std=c11",
+           "-I", sysconfig.get_paths()["include"], "-I", os.path.join(ROOT, "include"), "-o", tmp,
+           EXT_SOURCE, "-L", PKG, "-lvitattn", "-Wl,-rpath,$ORIGIN"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    if verbose and (res.stdout + res.stderr).strip():
+        print(res.stdout + res.stderr, file=sys.stderr)
+    os.replace(tmp, ext)
+    return ext
+
+
 def build(verbose: bool = False) -> str:
     _hipcc(SOURCES, LIBRARY, verbose)
     _hipcc(PROBE_SOURCES, PROBE_LIBRARY, verbose)
+    _build_ext(verbose)
     return LIBRARY
 
 
