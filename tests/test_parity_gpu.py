@@ -82,11 +82,13 @@ def test_stress_logits_parity(dev, va, N, D):
 
 
 @pytest.mark.parametrize("B,H,N", [(1, 1, 729), (4, 16, 729), (96, 16, 64), (1, 48, 129),
-                                   (8, 16, 256), (12, 16, 200)])
+                                   (8, 16, 256), (12, 16, 200), (6, 16, 729)])
 def test_grid_shapes(dev, va, B, H, N):
     """Grids with every wave count the launcher picks, and uneven XCD splits.
-    The last two are split-key grids of 1024 and 1344 workgroups, several per
-    compute unit."""
+    (8, 16, 256) and (12, 16, 200) are split-key grids of 1024 and 1344
+    workgroups, several per compute unit; (6, 16, 729), one GPU's share of
+    48 images at 384 px over 8 GPUs, gives 576 one-item workgroups, more than
+    fit on the chip at once."""
     wl = Workload("t", "grid", B=B, N=N, H=H, D=72, layout=LAYOUT_PACKED, layers=1, kind="iid",
                   index=60)
     li = make_layer(wl, B * 1000 + N)
