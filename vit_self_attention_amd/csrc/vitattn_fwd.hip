@@ -9,8 +9,15 @@
 // online softmax in registers, so the N x N score matrix never reaches HBM.
 //
 // Work decomposition
-//   * one workgroup per (image, head, block of 32*NW queries); NW waves of
-//     64 lanes, each wave owning 32 queries;
+//   * work items of (image, head, block of 32*NW queries); NW waves of 64
+//     lanes, each wave owning 32 queries.  One workgroup per item; with at
+//     least two items per workgroup slot, two four-wave workgroups per
+//     compute unit loop over the items instead, fetching the next item's
+//     tiles while they finish the current one;
+//   * short sequences (2..4 key tiles) on small grids split the keys
+//     instead (kSplit): the four waves share one 32-query block, each
+//     reduces one key tile on its own, and the partial results merge
+//     through LDS;
 //   * keys in tiles of 64, fetched cooperatively with 128-bit direct-to-LDS
 //     loads into a ring of LDS stages (row-major K and V), three tiles ahead
 //     of the tile being reduced, one barrier per tile;
@@ -36,7 +43,9 @@
 //     weights that multiply V;
 //   * tails: keys >= N of the last tile are fetched as copies of key N-1
 //     (so row maxima are unchanged) and get zero weights; queries >= N run
-//     on zero rows and are never stored.
+//     on copies of query N-1 and are never stored, and a wave whose 32
+//     queries all lie past N skips the products (it still fetches its share
+//     of each tile and meets every barrier).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
