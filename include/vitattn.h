@@ -77,9 +77,11 @@ enum {
  *             must be NULL for the packed layout.
  *   out       device pointer, same format, written in full: [B][H][N][D] (separate)
  *             or [B][N][H][D] (packed).  Must not overlap any input.
- *   B, H, N   images, heads, tokens.  Any N >= 1 (not only tile multiples);
- *             B, H or N equal to 0 is an empty problem: returns VITATTN_OK
- *             and launches nothing (its pointers may then be NULL).
+ *   B, H, N   images, heads, tokens.  Any N >= 1 (not only tile multiples)
+ *             up to 2^24; B*H*N at most 2^40 and B*H*ceil(N/32) at most
+ *             2^30 (else VITATTN_ERR_TOO_LARGE).  B, H or N equal to 0 is
+ *             an empty problem: returns VITATTN_OK and launches nothing (its
+ *             pointers may then be NULL).
  *   D         head dimension: 64 or 72.
  *   scale     logit scale, any finite value (usually 1/sqrt(D)); 0 gives
  *             uniform attention.
@@ -99,6 +101,31 @@ enum {
  */
 int vitattn_fwd(const void* qkv_or_q, const void* k, const void* v, void* out, int B, int H,
                 int N, int D, float scale, int layout, void* stream);
+
+/*
+ * vitattn_fwd_shape -- describes the launch vitattn_fwd makes for these sizes
+ * on the current device, without launching anything: how the (image, head,
+ * query) work is cut into work items and workgroups (the kernel's work
+ * decomposition follows the memory-aware tiling the Pi0 Flash Attention
+ * tutorial, section 1, credits for the speed-up).  For tests and benchmarks
+ * that name the kernel path they exercise.
+ *
+ *   waves       receives the waves of 64 lanes per workgroup: 1, 2 or 4.
+ *   split_keys  receives 1 when the waves of a workgroup share one block of
+ *               32 queries and split its keys (short sequences), else 0
+ *               (each wave then owns 32 queries of the block).
+ *   items       receives the number of work items (image, head, query block).
+ *   workgroups  receives the number of workgroups launched: one per item, or
+ *               fewer, each looping over several items.
+ *
+ * B, H, N, D and layout as for vitattn_fwd.  Errors: VITATTN_ERR_NULL_POINTER
+ * (an output pointer is NULL), and the size, head-dimension, layout and
+ * limit codes vitattn_fwd returns for the same sizes; nothing is written
+ * then.  With no usable device the count of compute units is unknown and
+ * the description is that of a launch with one workgroup per item.
+ */
+int vitattn_fwd_shape(int B, int H, int N, int D, int layout, int* waves, int* split_keys,
+                      int* items, int* workgroups);
 
 /*
  * Plans: a fixed sequence of forward calls recorded once into a HIP graph and

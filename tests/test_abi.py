@@ -54,7 +54,7 @@ def test_status_codes_match_header(va):
 
 
 def test_version_and_strerror(va):
-    assert va.version() == 100
+    assert va.version() == 200
     for name, code in _declared_enums().items():
         if name.startswith("VITATTN_ERR_"):
             msg = va.strerror(code)
@@ -326,3 +326,38 @@ def test_linear_empty_is_a_noop(va):
     assert _lin(va, M=0) == va.OK
     assert _lin(va, Nout=0) == va.OK
     assert _lin(va, M=0, x=0, out=0) == va.OK
+
+
+def test_fwd_shape_describes_the_launch_without_a_device(va):
+    """vitattn_fwd_shape on the CPU (no device: the compute-unit count is
+    unknown, so no workgroup loops): the split-key choice for short
+    sequences on small grids, and the largest wave count that still gives
+    512 workgroups."""
+    cases = {
+        # (B, H, N, D): (waves, split_keys, items)
+        (1, 12, 197, 64): (4, True, 12 * 7),     # 4 key tiles, 84 blocks of 32 queries
+        (3, 12, 101, 64): (4, True, 36 * 4),     # 2 key tiles
+        (2, 16, 256, 72): (4, True, 32 * 8),     # 4 key tiles
+        (1, 1, 64, 72): (1, False, 2),           # one key tile: never split
+        (1, 1, 729, 72): (1, False, 23),         # 12 key tiles, tiny grid
+        (8, 16, 257, 64): (2, False, 128 * 5),   # 4 waves would give 384 < 512 workgroups
+        (4, 16, 729, 72): (2, False, 64 * 12),
+        (6, 16, 729, 72): (4, False, 96 * 6),
+        (48, 16, 729, 72): (4, False, 768 * 6),
+        (64, 16, 256, 72): (4, False, 1024 * 2),  # 2048 blocks of 32: not split
+    }
+    for (B, H, N, D), (waves, split, items) in cases.items():
+        got = va.fwd_shape(B, H, N, D)
+        assert (got["waves"], got["split_keys"], got["items"]) == (waves, split, items), (B, H, N, D)
+        assert got["workgroups"] == items and not got["looping"]
+    for bad, code in (((1, 1, 8, 80), va._binding.ERR_UNSUPPORTED_D),
+                      ((-1, 1, 8, 64), va._binding.ERR_BAD_SIZE),
+                      ((1 << 20, 1 << 10, 1 << 10, 64), va._binding.ERR_TOO_LARGE)):
+        with pytest.raises(va.VitAttnError) as e:
+            va.fwd_shape(*bad)
+        assert e.value.status == code
+    rc = va._binding.lib.vitattn_fwd_shape(1, 1, 8, 64, 7, None, None, None, None)
+    assert rc == va._binding.ERR_NULL_POINTER
+    i = ctypes.c_int()
+    rc = va._binding.lib.vitattn_fwd_shape(1, 1, 8, 64, 7, *[ctypes.byref(i)] * 4)
+    assert rc == va._binding.ERR_BAD_LAYOUT

@@ -31,7 +31,7 @@ ERR_OVERLAP = -9
 ERR_GRAPH = -10
 ERR_UNSUPPORTED_SHAPE = -11
 
-EXPORTED = ("vitattn_fwd", "vitattn_linear", "vitattn_plan_create", "vitattn_plan_destroy",
+EXPORTED = ("vitattn_fwd", "vitattn_fwd_shape", "vitattn_linear", "vitattn_plan_create", "vitattn_plan_destroy",
             "vitattn_plan_launch", "vitattn_strerror", "vitattn_version")
 
 
@@ -62,6 +62,9 @@ def _load(path: str = LIBRARY):
     lib.vitattn_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.vitattn_linear.restype = ctypes.c_int
     lib.vitattn_linear.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.vitattn_fwd_shape.restype = ctypes.c_int
+    lib.vitattn_fwd_shape.argtypes = [ctypes.c_int] * 5 + [ip] * 4
     lib.vitattn_strerror.restype = ctypes.c_char_p
     lib.vitattn_strerror.argtypes = [ctypes.c_int]
     lib.vitattn_version.restype = ctypes.c_int
@@ -85,6 +88,20 @@ def fwd_raw(qkv_or_q: int, k: int | None, v: int | None, out: int, B: int, H: in
     """Direct call of vitattn_fwd with raw device addresses; returns the status."""
     return lib.vitattn_fwd(qkv_or_q or None, k or None, v or None, out or None, int(B), int(H),
                            int(N), int(D), float(scale), int(layout), stream or None)
+
+
+def fwd_shape(B: int, H: int, N: int, D: int, layout: int = LAYOUT_PACKED) -> dict:
+    """The launch vitattn_fwd makes for these sizes on the current device
+    (vitattn_fwd_shape): waves per workgroup, whether the waves split the
+    keys of one query block, work items and workgroups."""
+    vals = [ctypes.c_int() for _ in range(4)]
+    rc = lib.vitattn_fwd_shape(int(B), int(H), int(N), int(D), int(layout),
+                               *[ctypes.byref(x) for x in vals])
+    if rc != OK:
+        raise VitAttnError(rc, strerror(rc))
+    waves, split, items, wgs = (x.value for x in vals)
+    return {"waves": waves, "split_keys": bool(split), "items": items, "workgroups": wgs,
+            "looping": wgs < items}
 
 
 # vitattn_fwd itself, for the argument tuples fwd_args returns:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libvitattn.so")
 SOURCES = [os.path.join(CSRC, "vitattn_fwd.hip"), os.path.join(CSRC, "vitattn_linear.hip"),
-           os.path.join(CSRC, "vitattn_api.cpp")]
+           os.path.join(CSRC, "vitattn_api.cpp"), os.path.join(CSRC, "vitattn_host.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

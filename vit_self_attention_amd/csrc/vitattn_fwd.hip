@@ -1035,9 +1035,6 @@ int launch(const KernelArgs& ka, hipStream_t stream) {
 
 }  // namespace
 
-namespace {
-
-// compute units of the current device (0 if unknown), cached per device
 int compute_units() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
@@ -1053,36 +1050,19 @@ int compute_units() {
   return n;
 }
 
-}  // namespace
-
-int pick_waves(int B, int H, int N) {
-  // Short sequences (2..4 key tiles) on grids too small to fill the chip:
-  // four waves split the keys of one 32-query block (returned as -4).
-  const int64_t pairs = static_cast<int64_t>(B) * H;
-  const int ntiles = (N + 63) / 64;
-  if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 31) / 32) < 2048) return -4;
-  // Otherwise the largest workgroup (more K/V reuse per LDS tile) that still
-  // gives at least two workgroups per compute unit on the 256-CU part.
-  for (int nw = 4; nw > 1; nw >>= 1) {
-    const int64_t qblocks = (N + 32 * nw - 1) / (32 * nw);
-    if (pairs * qblocks >= 512) return nw;
-  }
-  return 1;
-}
-
 namespace {
 
 template <bool kF16>
-int launch_typed(const KernelArgs& ka, int D, int nw, hipStream_t s) {
+int launch_typed(const KernelArgs& ka, int D, const FwdShape& sh, hipStream_t s) {
   if (D == 64) {
-    if (nw == -4) return launch<64, 4, true, kF16>(ka, s);
-    if (nw == 4) return launch<64, 4, false, kF16>(ka, s);
-    if (nw == 2) return launch<64, 2, false, kF16>(ka, s);
+    if (sh.split) return launch<64, 4, true, kF16>(ka, s);
+    if (sh.waves == 4) return launch<64, 4, false, kF16>(ka, s);
+    if (sh.waves == 2) return launch<64, 2, false, kF16>(ka, s);
     return launch<64, 1, false, kF16>(ka, s);
   }
-  if (nw == -4) return launch<72, 4, true, kF16>(ka, s);
-  if (nw == 4) return launch<72, 4, false, kF16>(ka, s);
-  if (nw == 2) return launch<72, 2, false, kF16>(ka, s);
+  if (sh.split) return launch<72, 4, true, kF16>(ka, s);
+  if (sh.waves == 4) return launch<72, 4, false, kF16>(ka, s);
+  if (sh.waves == 2) return launch<72, 2, false, kF16>(ka, s);
   return launch<72, 1, false, kF16>(ka, s);
 }
 
@@ -1123,20 +1103,12 @@ int launch_fwd(const FwdArgs& f, void* stream) {
   const float abs_scale = f.scale < 0.f ? -f.scale : f.scale;
   ka.c = (abs_scale > 1e-30f ? abs_scale : 1e-30f) * kLog2e;
   ka.qsign = f.scale < 0.f ? 0x80008000u : 0u;
-  const int nw = pick_waves(f.B, f.H, f.N);
-  const int qpb = nw < 0 ? 32 : 32 * nw;  // queries per workgroup
-  ka.qblocks = (f.N + qpb - 1) / qpb;
-  ka.items = f.B * f.H * ka.qblocks;
-  ka.grid = ka.items;
-  if (nw == 4) {
-    // Two four-wave workgroups fit on a compute unit.  With more items than
-    // that, exactly that many workgroups loop over the items, fetching the
-    // next item's key tiles while they finish the current one.
-    const int slots = 2 * compute_units();
-    if (slots >= 16 && slots % 8 == 0 && ka.items >= 2 * slots) ka.grid = slots;
-  }
+  const FwdShape sh = fwd_shape(f.B, f.H, f.N, compute_units());
+  ka.qblocks = sh.qblocks;
+  ka.items = sh.items;
+  ka.grid = sh.grid;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return f.f16 ? launch_typed<true>(ka, f.D, nw, s) : launch_typed<false>(ka, f.D, nw, s);
+  return f.f16 ? launch_typed<true>(ka, f.D, sh, s) : launch_typed<false>(ka, f.D, sh, s);
 }
 
 }  // namespace vitattn

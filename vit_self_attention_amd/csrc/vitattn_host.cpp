@@ -1,0 +1,226 @@
+// Host-only part of libvitattn: argument checking for every entry point and
+// the launch shape of the attention kernel.  Plain C++ with no HIP header,
+// so that it builds with the host compiler alone (the CPU tests build it
+// with address and undefined-behaviour sanitizers and drive every check).
+//
+// The checks follow the boundary the Pi0 Flash Attention tutorial sets for
+// the swapped-in attention (section 3.2: the block's fused qkv activation
+// in, the same output as before; section 5.2: a mismatched argument is an
+// error, not a silent fallback): every argument is checked before any device
+// work and a failed check returns its negative status code.
+#include <math.h>
+#include <stdint.h>
+
+#include "vitattn.h"
+#include "vitattn_internal.h"
+
+namespace vitattn {
+
+namespace {
+
+constexpr int kVersion = 10000 * 0 + 100 * 2 + 0;  // 0.2.0
+constexpr int kMaxTokens = 1 << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + a_bytes) and [b, b + b_bytes) share a byte
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(b_bytes) && b0 < a0 + static_cast<uintptr_t>(a_bytes);
+}
+
+}  // namespace
+
+int check_fwd_limits(int B, int H, int N, int D, int layout) {
+  if (B <= 0 || H <= 0 || N <= 0) return VITATTN_OK;  // empty, or rejected earlier
+  // Element offsets are 64-bit in the kernel, and the (b, h, token) rows
+  // number at most 2^40 (every product below then stays far inside int64;
+  // B*H is formed first, below 2^62, and compared before it meets N).
+  // The kernel's token arithmetic is 32-bit: N stays far below 2^31.
+  if (N > kMaxTokens) return VITATTN_ERR_TOO_LARGE;
+  const int64_t pairs = static_cast<int64_t>(B) * H;
+  if (pairs > (int64_t(1) << 40) / N) return VITATTN_ERR_TOO_LARGE;
+  // A key tile (64 token rows) must span less than 2 GiB: the kernel
+  // addresses its rows with 32-bit byte offsets.
+  const int64_t token_stride =
+      layout == VITATTN_LAYOUT_PACKED_BN3HD ? 3 * static_cast<int64_t>(H) * D : D;
+  if (64 * token_stride * 2 >= (int64_t(1) << 31)) return VITATTN_ERR_TOO_LARGE;
+  // the work items, one per (image, head, block of 32 queries), must fit a
+  // 32-bit count
+  if (pairs * ((static_cast<int64_t>(N) + 31) / 32) > (int64_t(1) << 30)) return VITATTN_ERR_TOO_LARGE;
+  return VITATTN_OK;
+}
+
+int check_fwd(const void* qkv_or_q, const void* k, const void* v, void* out, int B, int H, int N,
+              int D, float scale, int layout, FwdArgs* a, bool* empty) {
+  *empty = false;
+  const bool f16 = (layout & VITATTN_DTYPE_FP16) != 0;
+  layout &= ~VITATTN_DTYPE_FP16;
+  if (layout != VITATTN_LAYOUT_SEPARATE_BHND && layout != VITATTN_LAYOUT_PACKED_BN3HD)
+    return VITATTN_ERR_BAD_LAYOUT;
+  if (layout == VITATTN_LAYOUT_PACKED_BN3HD && (k != nullptr || v != nullptr))
+    return VITATTN_ERR_BAD_LAYOUT;
+  if (B < 0 || H < 0 || N < 0) return VITATTN_ERR_BAD_SIZE;
+  if (D != 64 && D != 72) return VITATTN_ERR_UNSUPPORTED_D;
+  if (!isfinite(scale)) return VITATTN_ERR_BAD_SCALE;
+  // An empty problem has nothing to read or write; its buffers may be NULL
+  // (a zero-element tensor usually has no storage).
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return VITATTN_OK;
+  }
+  if (!qkv_or_q || !out) return VITATTN_ERR_NULL_POINTER;
+  if (layout == VITATTN_LAYOUT_SEPARATE_BHND && (!k || !v)) return VITATTN_ERR_NULL_POINTER;
+  if (!aligned16(qkv_or_q) || !aligned16(out)) return VITATTN_ERR_MISALIGNED;
+  if (layout == VITATTN_LAYOUT_SEPARATE_BHND && (!aligned16(k) || !aligned16(v)))
+    return VITATTN_ERR_MISALIGNED;
+
+  {
+    const int st = check_fwd_limits(B, H, N, D, layout);
+    if (st != VITATTN_OK) return st;
+  }
+  const int64_t rows = static_cast<int64_t>(B) * H * N;  // (b, h, token) rows, at most 2^40
+  const int64_t t_bytes = rows * D * 2;  // one of Q, K, V or O, in bytes
+  if (layout == VITATTN_LAYOUT_PACKED_BN3HD) {
+    if (overlaps(out, t_bytes, qkv_or_q, 3 * t_bytes)) return VITATTN_ERR_OVERLAP;
+  } else {
+    if (overlaps(out, t_bytes, qkv_or_q, t_bytes) || overlaps(out, t_bytes, k, t_bytes) ||
+        overlaps(out, t_bytes, v, t_bytes))
+      return VITATTN_ERR_OVERLAP;
+  }
+
+  *a = FwdArgs{};
+  a->B = B;
+  a->H = H;
+  a->N = N;
+  a->D = D;
+  a->scale = scale;
+  a->f16 = f16;
+  a->o = static_cast<uint16_t*>(out);
+  const int64_t hd = static_cast<int64_t>(H) * D;
+  if (layout == VITATTN_LAYOUT_PACKED_BN3HD) {
+    const uint16_t* base = static_cast<const uint16_t*>(qkv_or_q);
+    a->q = base;
+    a->k = base + hd;
+    a->v = base + 2 * hd;
+    const int64_t st = 3 * hd, sb = static_cast<int64_t>(N) * st;
+    a->q_sb = a->k_sb = a->v_sb = sb;
+    a->q_sh = a->k_sh = a->v_sh = D;
+    a->q_st = a->k_st = a->v_st = st;
+    a->o_sb = static_cast<int64_t>(N) * hd;
+    a->o_sh = D;
+    a->o_st = hd;
+  } else {
+    a->q = static_cast<const uint16_t*>(qkv_or_q);
+    a->k = static_cast<const uint16_t*>(k);
+    a->v = static_cast<const uint16_t*>(v);
+    const int64_t sh = static_cast<int64_t>(N) * D, sb = static_cast<int64_t>(H) * sh;
+    a->q_sb = a->k_sb = a->v_sb = a->o_sb = sb;
+    a->q_sh = a->k_sh = a->v_sh = a->o_sh = sh;
+    a->q_st = a->k_st = a->v_st = a->o_st = D;
+  }
+  return VITATTN_OK;
+}
+
+int check_linear(const void* x, const void* w, const void* bias, const void* residual, void* out,
+                 int M, int K, int Nout, int flags, LinearCall* c, bool* empty) {
+  *empty = false;
+  if ((flags & ~VITATTN_DTYPE_FP16) != 0) return VITATTN_ERR_BAD_LAYOUT;
+  if (M < 0 || K < 0 || Nout < 0) return VITATTN_ERR_BAD_SIZE;
+  if (K == 0 || K % 32 != 0 || Nout % 8 != 0) return VITATTN_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || Nout == 0) {
+    *empty = true;
+    return VITATTN_OK;
+  }
+  if (!x || !w || !out) return VITATTN_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (bias && !aligned16(bias)) ||
+      (residual && !aligned16(residual)))
+    return VITATTN_ERR_MISALIGNED;
+  // The kernel addresses x and w rows with 32-bit byte offsets.  Element
+  // counts are products of two ints (below 2^62) and are compared before
+  // they are turned into bytes.
+  const int64_t x_elems = static_cast<int64_t>(M) * K, w_elems = static_cast<int64_t>(Nout) * K;
+  if (x_elems >= (int64_t(1) << 31) || w_elems >= (int64_t(1) << 31)) return VITATTN_ERR_TOO_LARGE;
+  const int64_t o_elems = static_cast<int64_t>(M) * Nout;
+  if (o_elems >= (int64_t(1) << 39)) return VITATTN_ERR_TOO_LARGE;
+  const int64_t x_bytes = 2 * x_elems, w_bytes = 2 * w_elems, o_bytes = 2 * o_elems;
+  if (overlaps(out, o_bytes, x, x_bytes) || overlaps(out, o_bytes, w, w_bytes) ||
+      overlaps(out, o_bytes, bias, static_cast<int64_t>(Nout) * 2))
+    return VITATTN_ERR_OVERLAP;
+  // the residual may be the output itself (an in-place residual add: every
+  // element is read and written by the same lane), but not a shifted view
+  if (residual && residual != out && overlaps(out, o_bytes, residual, o_bytes)) return VITATTN_ERR_OVERLAP;
+  *c = LinearCall{};
+  c->x = static_cast<const uint16_t*>(x);
+  c->w = static_cast<const uint16_t*>(w);
+  c->bias = static_cast<const uint16_t*>(bias);
+  c->residual = static_cast<const uint16_t*>(residual);
+  c->out = static_cast<uint16_t*>(out);
+  c->M = M;
+  c->K = K;
+  c->Nout = Nout;
+  c->f16 = (flags & VITATTN_DTYPE_FP16) != 0;
+  return VITATTN_OK;
+}
+
+FwdShape fwd_shape(int B, int H, int N, int compute_units) {
+  FwdShape s{};
+  const int64_t pairs = static_cast<int64_t>(B) * H;
+  const int64_t ntiles = (static_cast<int64_t>(N) + 63) / 64;
+  // Short sequences (2..4 key tiles of 64) on grids too small to fill the
+  // chip: the four waves of a workgroup split the keys of one 32-query
+  // block.
+  if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 31) / 32) < 2048) {
+    s.waves = 4;
+    s.split = true;
+    s.qblocks = (N + 31) / 32;  // N <= 256 here
+  } else {
+    // Otherwise the largest workgroup (more K/V reuse per LDS tile) that
+    // still gives at least two workgroups per compute unit on the 256-CU
+    // part.
+    s.waves = 1;
+    for (int nw = 4; nw > 1; nw >>= 1) {
+      const int64_t qb = (static_cast<int64_t>(N) + 32 * nw - 1) / (32 * nw);
+      if (pairs * qb >= 512) {
+        s.waves = nw;
+        break;
+      }
+    }
+    s.qblocks = static_cast<int>((static_cast<int64_t>(N) + 32 * s.waves - 1) / (32 * s.waves));
+  }
+  s.items = static_cast<int>(pairs * s.qblocks);
+  s.grid = s.items;
+  if (!s.split && s.waves == 4) {
+    // Two four-wave workgroups fit on a compute unit.  With at least two
+    // items per such slot, exactly that many workgroups loop over the
+    // items, fetching the next item's key tiles while they finish the
+    // current one.
+    const int slots = 2 * compute_units;
+    if (slots >= 16 && slots % 8 == 0 && s.items >= 2 * slots) s.grid = slots;
+  }
+  return s;
+}
+
+}  // namespace vitattn
+
+extern "C" const char* vitattn_strerror(int status) {
+  switch (status) {
+    case VITATTN_OK: return "success";
+    case VITATTN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case VITATTN_ERR_BAD_SIZE: return "B, H or N is negative";
+    case VITATTN_ERR_UNSUPPORTED_D: return "head dimension D must be 64 or 72";
+    case VITATTN_ERR_BAD_SCALE: return "scale must be finite";
+    case VITATTN_ERR_BAD_LAYOUT: return "unknown layout, or k/v passed with the packed layout";
+    case VITATTN_ERR_MISALIGNED: return "device pointers must be 16-byte aligned";
+    case VITATTN_ERR_TOO_LARGE: return "problem exceeds the launch limits";
+    case VITATTN_ERR_LAUNCH: return "kernel launch failed";
+    case VITATTN_ERR_OVERLAP: return "out overlaps an input buffer";
+    case VITATTN_ERR_GRAPH: return "recording or launching the HIP graph failed";
+    case VITATTN_ERR_UNSUPPORTED_SHAPE:
+      return "linear layer: K must be a positive multiple of 32 and Nout a multiple of 8";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int vitattn_version(void) { return vitattn::kVersion; }
