@@ -17,7 +17,10 @@
  * Numerics: bf16 inputs (or fp16 with VITATTN_DTYPE_FP16), fp32 accumulation
  * and softmax state, probabilities rounded to the input format (nearest
  * even) for the P V product, output in the input format rounded to nearest
- * even.
+ * even.  Inputs must be finite.  The softmax's running maximum is updated
+ * lazily (weights up to 2^32 before a rescale, 2^8 for fp16), so the fp32
+ * sums stay finite for |V| below about 2^128 / (N * 2^32) (1e26 at
+ * N = 729; fp16 values cannot reach the fp16 bound).
  * Results are deterministic: the same inputs give the same output bits.
  *
  * C ABI only: plain pointers and sizes.  The library allocates no device

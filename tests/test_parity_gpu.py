@@ -304,3 +304,28 @@ def test_errors_raise(dev, va):
     with pytest.raises(va.VitAttnError) as e:
         va.fwd(qkv, scale=float("nan"))
     assert e.value.status == va._binding.ERR_BAD_SCALE
+
+
+@pytest.mark.parametrize("D", [64, 72])
+def test_large_values_with_growing_row_maxima(dev, va, D):
+    """bf16 values near 2^66 (about 7e19) with row maxima that grow by some
+    40 (log2 units) per key tile, so the accumulator is rescaled tile after
+    tile: the weights stay below 2^32 before each rescale, the fp32 sums of
+    weight times value stay finite (with weights up to 2^64 they would
+    overflow), and the result scaled back by 2^-66 meets the bar."""
+    rng = np.random.default_rng(91)
+    B, N, H = 1, 600, 2
+    scale = 1 / math.sqrt(D)
+    q = rng.standard_normal((B, N, H, D)).astype(np.float32) * np.float32(0.5)
+    k = rng.standard_normal((B, N, H, D)).astype(np.float32) * np.float32(0.5)
+    # logit of key j grows by 40 / log2(e) per 64 keys along channel 0
+    step = 40.0 / 1.4426950408889634 / 64.0
+    q[..., 0] = 8.0
+    k[..., 0] = (np.arange(N, dtype=np.float32) * np.float32(step / (8.0 * scale)))[None, :, None]
+    v = rng.standard_normal((B, N, H, D)).astype(np.float32)
+    big = np.float32(2.0 ** 66)
+    li = LayerInputs(f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v * big))
+    got = run_gpu(li, LAYOUT_PACKED, scale, dev)
+    assert np.all(np.isfinite(got)), "non-finite output for large values"
+    ref = _oracle(li, LAYOUT_PACKED, scale)
+    assert_parity(got / 2.0 ** 66, ref / 2.0 ** 66, "values near 2^66, growing maxima")

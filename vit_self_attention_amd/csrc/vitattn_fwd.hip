@@ -36,7 +36,7 @@
 //     are issued while the exponentials of tile j run on the VALU, and the
 //     P V products of tile j overlap the row max of tile j+1;
 //   * online softmax in base 2 with a lazy running max: the accumulator is
-//     rescaled only when a row's max grows by more than 2^64;
+//     rescaled only when a row's max grows by more than 2^32 (fp16: 2^8);
 //   * D = 72: the P V product runs three 32-row output tiles (d 0..95); the
 //     spare row d = 72 reads a column of ones stored after each V row, so
 //     the softmax denominator comes out of the same MFMA from the same bf16
@@ -72,13 +72,15 @@ constexpr int kKStride = 72;          // K row stride in LDS (elements): 144 B
 constexpr float kLog2e = 1.4426950408889634f;
 // The running max is lazy: it moves (and the accumulator is rescaled) only
 // when a row's max grows by more than 2^lazy.  Weights then stay below
-// 2^lazy and row sums below N * 2^lazy, inside fp32 range, while rounding a
-// weight to 16 bits is relative and so independent of the shift.  bf16 has
-// fp32's exponent range (lazy = 64); fp16 tops out near 2^16, so its weights
-// are kept below 2^8 (and those under 2^-24 of the row max, negligible
-// against it, flush to zero).
+// 2^lazy and row sums below N * 2^lazy, while rounding a weight to 16 bits is
+// relative and so independent of the shift.  bf16 (fp32's exponent range):
+// lazy = 32, so the fp32 sums of weight times value stay finite for any
+// |V| below 2^128 / (N * 2^32), about 1e26 at N = 729 (measured: no cost
+// against 2^64 at 384 px or N = 2048).  fp16 tops out near 2^16, so its
+// weights are kept below 2^8 (and those under 2^-24 of the row max,
+// negligible against it, flush to zero).
 template <bool kF16>
-constexpr float lazy_bound() { return kF16 ? 8.0f : 64.0f; }
+constexpr float lazy_bound() { return kF16 ? 8.0f : 32.0f; }
 
 // What the kernel works with; it arrives as scalar kernel arguments (see
 // fwd_kernel) and the strides are derived from the layout in the kernel.
