@@ -497,6 +497,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       f_vb = a.v + bn * a.i_sb + hn * a.i_sh;
     }
   };
+  // The fetch of a steady step (see step): a tile of the item being fetched
+  // other than its last (so a full one), so none of fetch_next's checks (end
+  // of stream, tail rows, switch to the next item) can be taken.
+  auto fetch_steady = [&]() __attribute__((always_inline)) {
+    const char* gk = reinterpret_cast<const char*>(f_kb + static_cast<int64_t>(f_t * kBlockN) * a.i_st);
+    const char* gv = reinterpret_cast<const char*>(f_vb + static_cast<int64_t>(f_t * kBlockN) * a.i_st);
+    const uint32_t stage = lds_base + 2 * stage_of(f_s) * kStageElems;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int I = i * NW + wave;
+      if (i >= kMinPerWave && I >= kInstr) continue;
+      dma16(I < kKInstr ? gk : gv, f_off[i], stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512));
+    }
+    ++f_s;
+    ++f_t;
+  };
   // Waits until the fetches of all but the last `tiles_in_flight` (0 or 1)
   // tiles issued by this wave have landed (vector-memory counter only; a
   // wave issues at least kMinPerWave fetches per tile, and kLater other
@@ -615,9 +631,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // while the matrix core works.
   // j is the tile's index in its item, gs its index in the tile stream
   // (gs = j for the split kernel, whose stage of tile j is stage j).
+  // kSteady: a step in the middle of an item whose fetch is a tile of the
+  // same item other than its last (j + 4 < ntiles): the fetch, the write of
+  // the next stage's ones column and the wait at the end are then
+  // unconditional, with no branch and little scalar work.
   auto step = [&](int j, int gs, f32x16* cur, f32x16* nxt, auto kNextC, auto kRaggedC,
-                  auto kHalfC) __attribute__((always_inline)) {
+                  auto kHalfC, auto kSteadyC) __attribute__((always_inline)) {
+    constexpr bool kSteady = decltype(kSteadyC)::value;
     constexpr bool kNext = decltype(kNextC)::value;
+    static_assert(!kSteady || kNext, "steady steps have a next tile");
     constexpr bool kRagged = decltype(kRaggedC)::value;
     // kHalf (the item's last step only): the tile holds at most 32 keys, so
     // only its first 32-key block is weighted and multiplied into P V; its
@@ -625,7 +647,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     // earlier over both blocks.)
     constexpr bool kThisHalf = decltype(kHalfC)::value;
     static_assert(!(kThisHalf && kNext), "only the last step reduces a half tile");
-    if constexpr (!kSplit) {
+    if constexpr (kSteady) {
+      fetch_steady();
+      write_ones(stage_of(gs + 1));
+    } else if constexpr (!kSplit) {
       // stage (gs-1) % kStages held stream tile gs-1, whose reads all ended
       // before the last barrier; it is refilled with stream tile gs + kStages - 1
       fetch_next();
@@ -763,7 +788,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     }
     // stream tile gs+2 must have landed before the next step reads its K,
     // and every wave must be done with stage gs % kStages before it is refilled
-    if constexpr (!kSplit) {
+    if constexpr (kSteady) {
+      // tile gs+3 (fetched this step) stays in flight
+      wait_fetch_and_sync(1, NoLater{});
+    } else if constexpr (!kSplit) {
       if constexpr (kNext) {
         if (j == ntiles - 3 && gs + 3 < stream_len) {
           wait_fetch_and_sync(after(gs + 2, f_s - 1), std::integral_constant<int, 1>{});
@@ -858,8 +886,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       wait_vmcnt<kVInstr - kHalfFetch>();  // V rows 0..31 landed
       asm volatile("" ::: "memory");
       if (half == 0) write_ones(my);  // rows 0..31 (lane = row); rows 32..63 in the step
-      if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{}, False{});
-      else step(my, my, sa, sb, False{}, False{}, False{});
+      if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{}, False{}, False{});
+      else step(my, my, sa, sb, False{}, False{}, False{}, False{});
     }
     // ---- merge the partial results of the waves (each: running max m,
     // accumulator, and for D = 64 the partial row sum) through LDS.  Wave w
@@ -961,21 +989,29 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       mx = rowmax(sa);
     }
     int j = 0;
+    // steady pairs: step j fetches tile j + 3 of this item, which is then
+    // neither its last tile (so it is full) nor followed by the switch to the
+    // next item's tiles, for every j < ntiles - 4
+    const int steady_end = ntiles - 4;
+    for (; j + 1 < steady_end; j += 2) {
+      step(j, g0 + j, sa, sb, True{}, False{}, False{}, True{});
+      step(j + 1, g0 + j + 1, sb, sa, True{}, False{}, False{}, True{});
+    }
     for (; j + 2 < ntiles; j += 2) {
-      step(j, g0 + j, sa, sb, True{}, False{}, False{});
-      step(j + 1, g0 + j + 1, sb, sa, True{}, False{}, False{});
+      step(j, g0 + j, sa, sb, True{}, False{}, False{}, False{});
+      step(j + 1, g0 + j + 1, sb, sa, True{}, False{}, False{}, False{});
     }
     if (j + 1 < ntiles) {
-      step(j, g0 + j, sa, sb, True{}, False{}, False{});
-      if (half_tail) step(j + 1, g0 + j + 1, sb, sa, False{}, True{}, True{});
-      else if (ragged) step(j + 1, g0 + j + 1, sb, sa, False{}, True{}, False{});
-      else step(j + 1, g0 + j + 1, sb, sa, False{}, False{}, False{});
+      step(j, g0 + j, sa, sb, True{}, False{}, False{}, False{});
+      if (half_tail) step(j + 1, g0 + j + 1, sb, sa, False{}, True{}, True{}, False{});
+      else if (ragged) step(j + 1, g0 + j + 1, sb, sa, False{}, True{}, False{}, False{});
+      else step(j + 1, g0 + j + 1, sb, sa, False{}, False{}, False{}, False{});
     } else {
       // (an odd tile count or a single tile: this tile's Q K^T ran in the
       // loop or before it)
-      if (half_tail) step(j, g0 + j, sa, sb, False{}, True{}, True{});
-      else if (ragged) step(j, g0 + j, sa, sb, False{}, True{}, False{});
-      else step(j, g0 + j, sa, sb, False{}, False{}, False{});
+      if (half_tail) step(j, g0 + j, sa, sb, False{}, True{}, True{}, False{});
+      else if (ragged) step(j, g0 + j, sa, sb, False{}, True{}, False{}, False{});
+      else step(j, g0 + j, sa, sb, False{}, False{}, False{}, False{});
     }
 
     // ---- epilogue: O = acc / l in bf16, rows < N only.  The tile goes
