@@ -499,17 +499,31 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   };
   // The fetch of a steady step (see step): a tile of the item being fetched
   // other than its last (so a full one), so none of fetch_next's checks (end
-  // of stream, tail rows, switch to the next item) can be taken.
-  auto fetch_steady = [&]() __attribute__((always_inline)) {
+  // of stream, tail rows, switch to the next item) can be taken.  The step
+  // issues this wave's instructions one at a time between its first matrix
+  // products (fetch_steady_one(i), i < kPerWave), then advances the stream
+  // (fetch_steady_done).  Issued together right after the barrier, the
+  // tile's 19 instructions queue at the compute unit's texture addresser
+  // and hold every wave for about a fifth of the step.  Waves without an
+  // i-th instruction repeat their first one into the sink, so every wave
+  // issues kPerWave of them with no branch (a branch in the chunk sequence
+  // lets the compiler sink the exponentials out of it).
+  auto fetch_steady_one = [&](int i) __attribute__((always_inline)) {
     const char* gk = reinterpret_cast<const char*>(f_kb + static_cast<int64_t>(f_t * kBlockN) * a.i_st);
     const char* gv = reinterpret_cast<const char*>(f_vb + static_cast<int64_t>(f_t * kBlockN) * a.i_st);
     const uint32_t stage = lds_base + 2 * stage_of(f_s) * kStageElems;
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int I = i * NW + wave;
-      if (i >= kMinPerWave && I >= kInstr) continue;
+    const int I = i * NW + wave;
+    if (i < kMinPerWave) {
       dma16(I < kKInstr ? gk : gv, f_off[i], stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512));
+    } else {
+      const bool real = I < kInstr;
+      const uint32_t sink = lds_base + 2 * kStages * kStageElems;
+      const char* src = real ? (I < kKInstr ? gk : gv) : (wave < kKInstr ? gk : gv);
+      dma16(src, real ? f_off[i] : f_off[0],
+            real ? stage + 2 * (I < kKInstr ? I * 512 : kKTile + (I - kKInstr) * 512) : sink);
     }
+  };
+  auto fetch_steady_done = [&]() __attribute__((always_inline)) {
     ++f_s;
     ++f_t;
   };
@@ -651,7 +665,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     constexpr bool kThisHalf = decltype(kHalfC)::value;
     static_assert(!(kThisHalf && kNext), "only the last step reduces a half tile");
     if constexpr (kSteady) {
-      fetch_steady();
       write_ones(stage_of(gs + 1));
     } else if constexpr (!kSplit) {
       // stage (gs-1) % kStages held stream tile gs-1, whose reads all ended
@@ -726,6 +739,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
             nxt[i & 1] = mma_32x32x8<kF16>(ko4[i - 8], qt, nxt[i & 1]);
 #pragma unroll
           for (int e = 24 * i / kQk; e < 24 * (i + 1) / kQk; ++e) do_exp(e);
+          // a steady step's fetch, spread evenly over the chunks
+          if constexpr (kSteady) {
+#pragma unroll
+            for (int f = 0; f < kPerWave; ++f)
+              if (f * kQk / kPerWave == i) fetch_steady_one(f);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -783,6 +802,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       }
     }
 
+    if constexpr (kSteady) {
+      if (!wave_active) {  // (a wave with no queries skipped the chunks above)
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) fetch_steady_one(i);
+      }
+      fetch_steady_done();
+    }
     if constexpr (!kSplit && !kNext) {
       // the item's last tile is reduced: start loading the next item's query
       // rows into qf, qt (after the last item this reloads that item's rows,
@@ -792,8 +818,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     // stream tile gs+2 must have landed before the next step reads its K,
     // and every wave must be done with stage gs % kStages before it is refilled
     if constexpr (kSteady) {
-      // tile gs+3 (fetched this step) stays in flight
-      wait_fetch_and_sync(1, NoLater{});
+      // tile gs+3 (fetched this step, kPerWave instructions from every
+      // wave) stays in flight
+      asm volatile("" ::: "memory");
+      wait_vmcnt<kPerWave>();
+      asm volatile("s_barrier" ::: "memory");
     } else if constexpr (!kSplit) {
       if constexpr (kNext) {
         if (j == ntiles - 3 && gs + 3 < stream_len) {
