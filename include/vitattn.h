@@ -54,7 +54,13 @@ enum {
   VITATTN_DTYPE_FP16 = 16
 };
 
-/* Status codes (0 = success; negative = error, nothing launched). */
+/* Status codes (0 = success; negative = error, nothing launched).  The
+ * failures the Pi0 Flash Attention tutorial lists for its attention swap
+ * (section 5.2 table: tensors on different devices, a missing or mismatched
+ * kernel library, a kernel image not built for the device) surface here as
+ * codes rather than exceptions: every argument is checked on the host
+ * before a launch, and a library without a gfx950 image for the current
+ * device returns VITATTN_ERR_LAUNCH. */
 enum {
   VITATTN_OK = 0,
   VITATTN_ERR_NULL_POINTER = -1,     /* a required pointer is NULL */
@@ -225,10 +231,15 @@ int vitattn_plan_destroy(vitattn_plan plan);
 int vitattn_linear(const void* x, const void* w, const void* bias, const void* residual,
                    void* out, int M, int K, int Nout, int flags, void* stream);
 
-/* Static description of a status code; never NULL. */
+/* A fixed English sentence for a status code ("unknown status" for any
+ * other value); static storage, never freed.  For the messages a caller
+ * shows when a call fails (Pi0 Flash Attention tutorial, section 5.2: each
+ * failure has a readable cause). */
 const char* vitattn_strerror(int status);
 
-/* Library version as 10000*major + 100*minor + patch. */
+/* Library version as 10000*major + 100*minor + patch, so that a caller can
+ * check which build it loaded (the same section 5.2 table traces an import
+ * failure to a library version mismatch). */
 int vitattn_version(void);
 
 #ifdef __cplusplus
