@@ -108,6 +108,39 @@ def test_long_sequence_looping_workgroups(dev, va, D):
     assert_parity(got, _oracle(li, LAYOUT_PACKED, wl.scale), f"long N=2048 D={D}")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("N,D", [(131071, 72), (100001, 64)])
+def test_very_long_sequence_sampled_rows(dev, va, N, D, fmt):
+    """One image, two heads, about 10^5 tokens: 1.5-2k key tiles per item
+    (streams far longer than any encoder's), ragged last key tiles of 63
+    and 33 keys and last query blocks of 127 and 33 rows, stress logits
+    (std ~8) with boosted rows; checked on sampled rows against the
+    oracle's row entry point."""
+    import torch
+    wl = Workload("t", "very long", B=1, N=N, H=2, D=D, layout=LAYOUT_PACKED, layers=1,
+                  kind="stress", index=80 + D)
+    assert va.fwd_shape(1, 2, N, D)["looping"]
+    li = make_layer(wl, 0, fmt=fmt)
+    arrs = li.in_layout(LAYOUT_PACKED)
+    dt = torch.float16 if fmt == "f16" else torch.bfloat16
+    qkv = torch.from_numpy(np.ascontiguousarray(arrs[0]).view(np.int16)).view(dt).to(dev)
+    print(f"[very long] N={N} D={D} {fmt}", flush=True)
+    o = va.fwd(qkv, scale=wl.scale)
+    torch.cuda.synchronize(dev)
+    got = logical(o, LAYOUT_PACKED)
+    rng = np.random.default_rng(81 + D)
+    R = 96
+    rows = np.stack([np.zeros(R, np.int64), rng.integers(0, 2, R), rng.integers(0, N, R)], 1)
+    rows[:6, 2] = [0, 1, 63, 64, N - 2, N - 1]
+    ref = oracle.attention_rows(*arrs, LAYOUT_PACKED, 1, 2, N, D, wl.scale, rows, fmt=fmt)
+    got_rows = np.stack([got[b, i, h] for b, h, i in rows])
+    assert np.all(np.isfinite(got_rows))
+    err = np.abs(got_rows - ref)
+    tmax, tmean = (1e-2, 1e-3) if fmt == "f16" else (2e-2, 2e-3)
+    print(f"[very long] N={N} D={D} {fmt}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}", flush=True)
+    assert err.max() <= tmax and err.mean() <= tmean
+
+
 def test_separate_layout_full_size_sampled_rows(dev, va):
     """The 384 px workload's shape and values in the separate [B,H,N,D]
     layout, run by the looping-workgroup kernel, checked on 256 sampled
