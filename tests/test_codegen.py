@@ -100,3 +100,28 @@ def test_linear_kernels_m0_and_registers(linear_asm):
                 assert body[i + 1] == "s_nop 0" and body[i + 2].startswith("global_load_lds_dwordx4")
         assert int(re.search(r"ScratchSize: (\d+)", meta).group(1)) == 0, name
         assert int(re.search(r"TotalNumVgprs: (\d+)", meta).group(1)) <= 256, name
+
+
+def test_small_division_is_exact_over_its_range():
+    """The kernels divide item and head indices with div_small:
+    floor(fma(n, rcp(d), 2^-12)) in fp32, for 0 <= n < 2048 and
+    1 <= d < 2048 (fewer than 2048 items).  Checked here for every such n
+    and d, with the reciprocal correctly rounded and up to two ulp either
+    side of 1/d (v_rcp_f32 is accurate to one ulp), the fma rounded once."""
+    import numpy as np
+    n = np.arange(0, 2048, dtype=np.int64)
+    nf = n.astype(np.float64)
+    for d in range(1, 2048):
+        r0 = np.float32(1.0) / np.float32(d)
+        rs = [r0]
+        lo = hi = r0
+        for _ in range(2):
+            lo = np.nextafter(lo, np.float32(0), dtype=np.float32)
+            hi = np.nextafter(hi, np.float32(1), dtype=np.float32)
+            rs += [lo, hi]
+        for r in rs:
+            # n * r is exact in float64 (24-bit by 11-bit significands); one
+            # rounding of n * r + 2^-12 to fp32 is the fma
+            x = (nf * np.float64(r) + 2.0 ** -12).astype(np.float32)
+            q = x.astype(np.int64)  # truncation, as v_cvt_i32_f32
+            assert np.array_equal(q, n // d), (d, float(r))

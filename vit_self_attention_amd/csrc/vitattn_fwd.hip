@@ -227,6 +227,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// n / d for 0 <= n < 2048 and 1 <= d < 2048, as floor(n * rcp(d) + 2^-12)
+// with the hardware reciprocal (v_rcp_f32, within an ulp): a handful of VALU
+// operations in place of the thirty-odd dependent instructions of a general
+// 32-bit division, which sit at the start of every workgroup.  Over that
+// range the reciprocal's error and the bias stay below the distance 1/d
+// from n/d up to the next integer, so the floor is exact (checked for every
+// such n and d, with reciprocals up to two ulp from 1/d, by the host tests).
+__device__ __forceinline__ int div_small(int n, int d) {
+  return static_cast<int>(
+      __builtin_fmaf(static_cast<float>(n), __builtin_amdgcn_rcpf(static_cast<float>(d)), 0x1p-12f));
+}
+
 // Workgroup id -> logical tile id.  Workgroups are dispatched round-robin
 // over the 8 XCDs (id mod 8); this bijection gives each XCD a contiguous
 // range of logical tiles, so the query blocks of one (image, head) -- which
@@ -354,6 +366,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     if (single) return it0;
     return r < ky ? lo + r * gx + lx : lo + ky * gx + (r - ky) * (gx / 2) + lx;
   };
+  // (image, head, query block) of an item
   auto coords = [&](int item, int& bi, int& hi_, int& qbi) {
     const int bh = item / a.qblocks;
     qbi = item - bh * a.qblocks;
@@ -361,7 +374,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     hi_ = bh - bi * a.H;
   };
   int b, h, qb;
-  coords(it0, b, h, qb);
+  // the first item's, on the path to the first fetch: below 2048 items
+  // every quotient is a small one (the split kernel only runs below that
+  // count)
+  if (kSplit || a.items < 2048) {
+    // two independent quotients (qblocks * H <= items): their latencies overlap
+    const int bh = div_small(it0, a.qblocks);
+    b = div_small(it0, a.qblocks * a.H);
+    qb = it0 - bh * a.qblocks;
+    h = bh - b * a.H;
+  } else {
+    coords(it0, b, h, qb);
+  }
   const uint16_t* kbase = a.k + b * a.i_sb + h * a.i_sh;
   const uint16_t* vbase = a.v + b * a.i_sb + h * a.i_sh;
 

@@ -170,7 +170,8 @@ FwdShape fwd_shape(int B, int H, int N, int compute_units) {
   const int64_t ntiles = (static_cast<int64_t>(N) + 63) / 64;
   // Short sequences (2..4 key tiles of 64) on grids too small to fill the
   // chip: the four waves of a workgroup split the keys of one 32-query
-  // block.
+  // block.  (Fewer than 2048 items: the kernel's coordinate arithmetic for
+  // this path is exact only below that count.)
   if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 31) / 32) < 2048) {
     s.waves = 4;
     s.split = true;
