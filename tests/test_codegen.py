@@ -125,3 +125,16 @@ def test_small_division_is_exact_over_its_range():
             x = (nf * np.float64(r) + 2.0 ** -12).astype(np.float32)
             q = x.astype(np.int64)  # truncation, as v_cvt_i32_f32
             assert np.array_equal(q, n // d), (d, float(r))
+
+
+def test_multiplier_division_is_exact_where_launch_allows_it():
+    """The split kernel divides by qblocks and H as (n * ceil(2^k / d)) >> k
+    (k = 16 and 20), with the multipliers computed on the host.  That is
+    n / d whenever n * d < 2^k, the condition launch checks; here for every
+    such n and d (d up to 2047)."""
+    import numpy as np
+    for k in (16, 20):
+        for d in range(1, 2048):
+            n = np.arange(0, -(-(1 << k) // d), dtype=np.int64)  # n * d < 2^k
+            m = -(-(1 << k) // d)
+            assert np.array_equal((n * m) >> k, n // d), (k, d)

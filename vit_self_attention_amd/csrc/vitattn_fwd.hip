@@ -264,15 +264,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // when the scale is negative (Q is then negated instead).  The strides
   // follow from the layout: separate [B,H,N,D] rows are D apart, packed
   // [B,N,3,H,D] rows 3*H*D, and the output is [B,H,N,D] or [B,N,H,D].
+  // The split kernel's qblocks and H carry, above their low 8 and 11 bits,
+  // the multipliers ceil(2^16 / qblocks) and ceil(2^20 / H) that divide by
+  // them (see launch).
+  const int qblocks_ = kSplit ? (qblocks & 0xff) : qblocks;
+  const int H_ = kSplit ? (H & 0x7ff) : H;
   KernelArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.i_st = i_st;
-  a.H = H;
+  a.H = H_;
   a.N = N_;
-  a.qblocks = qblocks;
+  a.qblocks = qblocks_;
   a.items = items;
   a.grid = grid;
   a.c = __builtin_fabsf(cs);
@@ -281,10 +286,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     const bool sep = i_st == D;
     const int64_t nd = static_cast<int64_t>(N_) * D;
     a.i_sh = sep ? nd : D;
-    a.i_sb = sep ? H * nd : static_cast<int64_t>(N_) * i_st;
-    a.o_sb = H * nd;
+    a.i_sb = sep ? H_ * nd : static_cast<int64_t>(N_) * i_st;
+    a.o_sb = H_ * nd;
     a.o_sh = sep ? nd : D;
-    a.o_st = sep ? D : H * D;
+    a.o_st = sep ? D : H_ * D;
   }
   constexpr bool kOnesRow = (D % 32) != 0;          // D = 72
   constexpr int kOutTiles = kOnesRow ? 3 : 2;
@@ -374,10 +379,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     hi_ = bh - bi * a.H;
   };
   int b, h, qb;
-  // the first item's, on the path to the first fetch: below 2048 items
-  // every quotient is a small one (the split kernel only runs below that
-  // count)
-  if (kSplit || a.items < 2048) {
+  // the first item's, on the path to the first fetch
+  if constexpr (kSplit) {
+    // q = (n * ceil(2^k / d)) >> k is n / d whenever n * d < 2^k: here
+    // item * qblocks <= 2^16 and (image, head) * H <= 2^20, and the 32-bit
+    // products do not overflow (launch checks all four)
+    const int bh = static_cast<int>((static_cast<uint32_t>(it0) * (static_cast<uint32_t>(qblocks) >> 8)) >> 16);
+    b = static_cast<int>((static_cast<uint32_t>(bh) * (static_cast<uint32_t>(H) >> 11)) >> 20);
+    qb = it0 - bh * a.qblocks;
+    h = bh - b * a.H;
+  } else if (a.items < 2048) {
+    // below 2048 items every quotient is a small one
     // two independent quotients (qblocks * H <= items): their latencies overlap
     const int bh = div_small(it0, a.qblocks);
     b = div_small(it0, a.qblocks * a.H);
@@ -1122,8 +1134,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
 
 template <int D, int NW, bool kSplit, bool kF16>
 int launch(const KernelArgs& ka, hipStream_t stream) {
+  int qblocks = ka.qblocks, H = ka.H;
+  if constexpr (kSplit) {
+    // the split kernel divides by qblocks and H with multipliers packed
+    // above them: exact while items * qblocks <= 2^16 and pairs * H <= 2^20,
+    // and the products item * mq and pair * mh must fit in 32 bits (the
+    // split path has fewer than 2048 items and at most 8 query blocks)
+    if (ka.qblocks < 1 || ka.qblocks > 255 || H < 1 || H > 2047) return VITATTN_ERR_LAUNCH;
+    const int64_t pairs = ka.items / ka.qblocks;
+    const int64_t mq = ((int64_t(1) << 16) + ka.qblocks - 1) / ka.qblocks;
+    const int64_t mh = ((int64_t(1) << 20) + H - 1) / H;
+    if (static_cast<int64_t>(ka.items) * ka.qblocks > (int64_t(1) << 16) || pairs * H > (int64_t(1) << 20) ||
+        ka.items * mq >= (int64_t(1) << 32) || pairs * mh >= (int64_t(1) << 32))
+      return VITATTN_ERR_LAUNCH;
+    qblocks = static_cast<int>(static_cast<uint32_t>(ka.qblocks) | (static_cast<uint32_t>(mq) << 8));
+    H = static_cast<int>(static_cast<uint32_t>(H) | (static_cast<uint32_t>(mh) << 11));
+  }
   hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit, kF16>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka.grid,
-                     ka.qblocks, ka.H, ka.N, ka.i_st, ka.qsign ? -ka.c : ka.c, ka.q, ka.k, ka.v, ka.o, ka.items);
+                     qblocks, H, ka.N, ka.i_st, ka.qsign ? -ka.c : ka.c, ka.q, ka.k, ka.v, ka.o, ka.items);
   return hipGetLastError() == hipSuccess ? VITATTN_OK : VITATTN_ERR_LAUNCH;
 }
 
