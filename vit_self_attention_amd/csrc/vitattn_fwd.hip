@@ -231,9 +231,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // with the hardware reciprocal (v_rcp_f32, within an ulp): a handful of VALU
 // operations in place of the thirty-odd dependent instructions of a general
 // 32-bit division, which sit at the start of every workgroup.  Over that
-// range the reciprocal's error and the bias stay below the distance 1/d
-// from n/d up to the next integer, so the floor is exact (checked for every
-// such n and d, with reciprocals up to two ulp from 1/d, by the host tests).
+// range the bias exceeds the product's error, so an exact quotient is not
+// rounded down, and bias plus error stay below 1/d, the least distance from
+// a non-integer n/d up to the next integer: the floor is exact (checked for
+// every such n and d, with reciprocals up to two ulp from 1/d, by the host
+// tests).
 __device__ __forceinline__ int div_small(int n, int d) {
   return static_cast<int>(
       __builtin_fmaf(static_cast<float>(n), __builtin_amdgcn_rcpf(static_cast<float>(d)), 0x1p-12f));
@@ -382,15 +384,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // the first item's, on the path to the first fetch
   if constexpr (kSplit) {
     // q = (n * ceil(2^k / d)) >> k is n / d whenever n * d < 2^k: here
-    // item * qblocks <= 2^16 and (image, head) * H <= 2^20, and the 32-bit
-    // products do not overflow (launch checks all four)
+    // every item * qblocks < 2^16 and (image, head) * H < 2^20, and the
+    // 32-bit products do not overflow (launch checks both)
     const int bh = static_cast<int>((static_cast<uint32_t>(it0) * (static_cast<uint32_t>(qblocks) >> 8)) >> 16);
     b = static_cast<int>((static_cast<uint32_t>(bh) * (static_cast<uint32_t>(H) >> 11)) >> 20);
     qb = it0 - bh * a.qblocks;
     h = bh - b * a.H;
   } else if (a.items < 2048) {
-    // below 2048 items every quotient is a small one
-    // two independent quotients (qblocks * H <= items): their latencies overlap
+    // below 2048 items every quotient is a small one; the two quotients
+    // (qblocks * H <= items) are independent, so their latencies overlap
     const int bh = div_small(it0, a.qblocks);
     b = div_small(it0, a.qblocks * a.H);
     qb = it0 - bh * a.qblocks;
