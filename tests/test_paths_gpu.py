@@ -34,6 +34,14 @@ PATHS = [
     ("split64_vitb160x3", 3, 12, 101, 64, LAYOUT_PACKED, "iid", (4, True, False)),
     # split keys, D = 72: SigLIP at 224 px x 2 (4 key tiles)
     ("split72_siglip224x2", 2, 16, 256, 72, LAYOUT_PACKED, "gamma", (4, True, False)),
+    # split keys with many heads and several images: the first item's
+    # coordinates come from multiply-shift divisions by qblocks and H (2040
+    # and 1530 items, H not a power of two)
+    ("split64_170heads_x3", 3, 170, 100, 64, LAYOUT_SEPARATE, "iid", (4, True, False)),
+    ("split72_255heads_x2", 2, 255, 96, 72, LAYOUT_PACKED, "gamma", (4, True, False)),
+    # one wave per workgroup: ViT-B/16 at 384 px x 4 (12 heads, 19 query
+    # blocks, 912 items)
+    ("nw1_vitb384x4", 4, 12, 577, 64, LAYOUT_PACKED, "iid", (1, False, False)),
     # one wave per workgroup (a single image and head: 23 items)
     ("nw1_d64", 1, 1, 729, 64, LAYOUT_PACKED, "stress", (1, False, False)),
     ("nw1_d72", 1, 1, 729, 72, LAYOUT_PACKED, "stress", (1, False, False)),
