@@ -11,9 +11,10 @@
 // Work decomposition
 //   * work items of (image, head, block of 32*NW queries); NW waves of 64
 //     lanes, each wave owning 32 queries.  One workgroup per item; with at
-//     least two items per workgroup slot, two four-wave workgroups per
-//     compute unit loop over the items instead, fetching the next item's
-//     tiles while they finish the current one;
+//     least two items per workgroup slot (or more than one and at most one
+//     and a half), two four-wave workgroups per compute unit loop over the
+//     items instead, fetching the next item's tiles while they finish the
+//     current one;
 //   * short sequences (2..4 key tiles) on small grids split the keys
 //     instead (kSplit): the four waves share one 32-query block, each
 //     reduces one key tile on its own, and the partial results merge
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // unit, the one dispatched first (block < grid/2) wins most issue
   // conflicts and runs about 1.2 times faster: the last rounds, past
   // 0.9 times the average number of items, go to those workgroups only.
-  // (The host loops only with at least two items per workgroup.)
+  // (The host loops with at least two items per workgroup, or with at most
+  // one and a half: then each of those workgroups takes at most one more.)
   int it0 = 0, lo = 0, gx = 1, ky = 1, lx = 0;
   bool single = true;
   int nitems = 1;
