@@ -96,8 +96,8 @@ int main() {
   shape("shape_c5", 48, 16, 729, 256);
   shape("shape_c5_no_device", 48, 16, 729, 0);
   shape("shape_384x6", 6, 16, 729, 256);    // 1.125 items per slot: loops
-  shape("shape_384x8", 8, 16, 729, 256);    // 1.5 items per slot: loops
-  shape("shape_384x9", 9, 16, 729, 256);    // 1.6875: one workgroup per item
+  shape("shape_384x9", 9, 16, 729, 256);    // 1.6875 items per slot: loops
+  shape("shape_n1024x4", 4, 16, 1024, 256); // one item per slot: one workgroup each
   shape("shape_one_token", 1, 1, 1, 256);
   shape("shape_max_n", 1, 1, 1 << 24, 256);
   // status strings: every code has one, unknown codes a fixed text

@@ -51,15 +51,17 @@ PATHS = [
     # two waves per workgroup: 384 px x 4 images (768 items)
     ("nw2_384x4_d64", 4, 16, 729, 64, LAYOUT_PACKED, "stress", (2, False, False)),
     ("nw2_384x4_d72", 4, 16, 729, 72, LAYOUT_PACKED, "stress", (2, False, False)),
-    # four waves, one workgroup per item: 9 images at 384 px (864 items,
-    # more than one and a half per workgroup slot)
-    ("nw4_one_384x9_d64", 9, 16, 729, 64, LAYOUT_PACKED, "stress", (4, False, False)),
-    ("nw4_one_384x9_d72", 9, 16, 729, 72, LAYOUT_PACKED, "stress", (4, False, False)),
-    # four-wave looping workgroups with at most one more item each: one
-    # GPU's share (6 images) of the 48-image 384 px call over 8 GPUs (576
-    # items on 512 workgroups)
+    # four waves, one workgroup per item: as many items as workgroup slots
+    # (4 images, N = 1024: 512 items)
+    ("nw4_one_n1024x4_d64", 4, 16, 1024, 64, LAYOUT_PACKED, "stress", (4, False, False)),
+    ("nw4_one_n1024x4_d72", 4, 16, 1024, 72, LAYOUT_PACKED, "stress", (4, False, False)),
+    # four-wave looping workgroups taking one or two items each: one GPU's
+    # share (6 images) of the 48-image 384 px call over 8 GPUs (576 items
+    # on 512 workgroups), and 9 images (864 items: a second item for the
+    # younger workgroups too)
     ("loop_384x6_d64", 6, 16, 729, 64, LAYOUT_PACKED, "stress", (4, False, True)),
     ("loop_384x6_d72", 6, 16, 729, 72, LAYOUT_PACKED, "stress", (4, False, True)),
+    ("loop_384x9_d72", 9, 16, 729, 72, LAYOUT_SEPARATE, "stress", (4, False, True)),
     # four-wave looping workgroups: ViT-L/14 at 224 px x 24 (1152 items) and
     # 384 px x 12 (1152 items), and a one-tile sequence (N = 64, 1536 items)
     ("loop_vitl224x24", 24, 16, 257, 64, LAYOUT_PACKED, "iid", (4, False, True)),

@@ -51,8 +51,8 @@ SHAPES = {
     "shape_c5": "waves=4 split=0 qblocks=6 items=4608 grid=512",
     "shape_c5_no_device": "waves=4 split=0 qblocks=6 items=4608 grid=4608",
     "shape_384x6": "waves=4 split=0 qblocks=6 items=576 grid=512",
-    "shape_384x8": "waves=4 split=0 qblocks=6 items=768 grid=512",
-    "shape_384x9": "waves=4 split=0 qblocks=6 items=864 grid=864",
+    "shape_384x9": "waves=4 split=0 qblocks=6 items=864 grid=512",
+    "shape_n1024x4": "waves=4 split=0 qblocks=8 items=512 grid=512",
     "shape_one_token": "waves=1 split=0 qblocks=1 items=1 grid=1",
     "shape_max_n": "waves=4 split=0 qblocks=131072 items=131072 grid=512",
 }

@@ -10,11 +10,10 @@
 //
 // Work decomposition
 //   * work items of (image, head, block of 32*NW queries); NW waves of 64
-//     lanes, each wave owning 32 queries.  One workgroup per item; with at
-//     least two items per workgroup slot (or more than one and at most one
-//     and a half), two four-wave workgroups per compute unit loop over the
-//     items instead, fetching the next item's tiles while they finish the
-//     current one;
+//     lanes, each wave owning 32 queries.  One workgroup per item; with
+//     more items than four-wave workgroup slots, two four-wave workgroups
+//     per compute unit loop over the items instead, fetching the next
+//     item's tiles while they finish the current one;
 //   * short sequences (2..4 key tiles) on small grids split the keys
 //     instead (kSplit): the four waves share one 32-query block, each
 //     reduces one key tile on its own, and the partial results merge
@@ -346,8 +345,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // unit, the one dispatched first (block < grid/2) wins most issue
   // conflicts and runs about 1.2 times faster: the last rounds, past
   // 0.9 times the average number of items, go to those workgroups only.
-  // (The host loops with at least two items per workgroup, or with at most
-  // one and a half: then each of those workgroups takes at most one more.)
+  // With fewer than two items per workgroup the second round is spread over
+  // all of them instead, the first dispatched first, so none takes three.
   int it0 = 0, lo = 0, gx = 1, ky = 1, lx = 0;
   bool single = true;
   int nitems = 1;
@@ -365,7 +364,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     if (ky > nx / gx) ky = nx / gx;
     it0 = lo + lx;
     nitems = ky;
-    if (lx < gx / 2) {
+    if (nx < 2 * gx) {
+      nitems = 1 + (lx < nx - gx ? 1 : 0);  // ky = 1: item_at(1) = lo + gx + lx
+    } else if (lx < gx / 2) {
       const int left = nx - ky * gx - lx;
       nitems += left > 0 ? (left + gx / 2 - 1) / (gx / 2) : 0;
     }

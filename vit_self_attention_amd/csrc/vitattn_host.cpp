@@ -193,20 +193,16 @@ FwdShape fwd_shape(int B, int H, int N, int compute_units) {
   s.items = static_cast<int>(pairs * s.qblocks);
   s.grid = s.items;
   if (!s.split && s.waves == 4) {
-    // Two four-wave workgroups fit on a compute unit.  With at least two
-    // items per such slot, exactly that many workgroups loop over the
-    // items, fetching the next item's key tiles while they finish the
-    // current one.  So do they with more than one and at most one and a
-    // half items per slot: the items left after the first round then go
-    // to the workgroups dispatched first, at most one more each, fetched
-    // while they finish their first (6 images at 384 px, 576 items: 29.4
-    // against 30.7 us as a second round of workgroups).  Beyond one and a
-    // half, some would take three items, and a second round of
-    // workgroups does better.
+    // Two four-wave workgroups fit on a compute unit.  With more items
+    // than such slots, exactly that many workgroups loop over the items,
+    // fetching the next item's key tiles while they finish the current
+    // one.  Below two items per slot each workgroup takes one or two, the
+    // first dispatched first, in place of a second round of workgroups: 6,
+    // 9 and 10 images at 384 px 29.4, 42.4 and 44.6 us against 30.7, 43.2
+    // and 45.9; ViT-L/14 at 16 and 20 images 15.2 and 18.9 against 16.7
+    // and 20.0.
     const int slots = 2 * compute_units;
-    if (slots >= 16 && slots % 8 == 0 &&
-        (s.items >= 2 * slots || (s.items > slots && 2 * static_cast<int64_t>(s.items) <= 3 * slots)))
-      s.grid = slots;
+    if (slots >= 16 && slots % 8 == 0 && s.items > slots) s.grid = slots;
   }
   return s;
 }
