@@ -39,18 +39,23 @@ PATHS = [
     # and 1530 items, H not a power of two)
     ("split64_170heads_x3", 3, 170, 100, 64, LAYOUT_SEPARATE, "iid", (4, True, False)),
     ("split72_255heads_x2", 2, 255, 96, 72, LAYOUT_PACKED, "gamma", (4, True, False)),
-    # one wave per workgroup: ViT-B/16 at 384 px x 4 (12 heads, 19 query
-    # blocks, 912 items)
-    ("nw1_vitb384x4", 4, 12, 577, 64, LAYOUT_PACKED, "iid", (1, False, False)),
+    # one wave per workgroup: ViT-B/16 at 384 px, one image (12 heads, 19
+    # query blocks: 228 items; two waves would give 120 workgroups)
+    ("nw1_vitb384x1", 1, 12, 577, 64, LAYOUT_PACKED, "iid", (1, False, False)),
     # one wave per workgroup (a single image and head: 23 items)
     ("nw1_d64", 1, 1, 729, 64, LAYOUT_PACKED, "stress", (1, False, False)),
     ("nw1_d72", 1, 1, 729, 72, LAYOUT_PACKED, "stress", (1, False, False)),
-    # two waves per workgroup: ViT-L/14 at 224 px, one view x 8 (640 items)
-    ("nw2_vitl224x8", 8, 16, 257, 64, LAYOUT_PACKED, "iid", (2, False, False)),
-    ("nw2_vitl224x8_d72", 8, 16, 257, 72, LAYOUT_PACKED, "iid", (2, False, False)),
-    # two waves per workgroup: 384 px x 4 images (768 items)
-    ("nw2_384x4_d64", 4, 16, 729, 64, LAYOUT_PACKED, "stress", (2, False, False)),
-    ("nw2_384x4_d72", 4, 16, 729, 72, LAYOUT_PACKED, "stress", (2, False, False)),
+    # two waves per workgroup: ViT-L/14 at 224 px, two views (160 items;
+    # four waves would give 96 workgroups)
+    ("nw2_vitl224x2", 2, 16, 257, 64, LAYOUT_PACKED, "iid", (2, False, False)),
+    ("nw2_vitl224x2_d72", 2, 16, 257, 72, LAYOUT_PACKED, "iid", (2, False, False)),
+    # two waves per workgroup: 384 px, one image (192 items)
+    ("nw2_384x1_d64", 1, 16, 729, 64, LAYOUT_PACKED, "stress", (2, False, False)),
+    ("nw2_384x1_d72", 1, 16, 729, 72, LAYOUT_PACKED, "stress", (2, False, False)),
+    # four waves, one workgroup per item, fewer workgroups than slots:
+    # ViT-L/14 at 224 px x 8 and 384 px x 4 (384 items each)
+    ("nw4_one_vitl224x8", 8, 16, 257, 64, LAYOUT_PACKED, "iid", (4, False, False)),
+    ("nw4_one_384x4_d72", 4, 16, 729, 72, LAYOUT_PACKED, "stress", (4, False, False)),
     # four waves, one workgroup per item: as many items as workgroup slots
     # (4 images, N = 1024: 512 items)
     ("nw4_one_n1024x4_d64", 4, 16, 1024, 64, LAYOUT_PACKED, "stress", (4, False, False)),

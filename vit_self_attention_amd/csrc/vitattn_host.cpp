@@ -177,13 +177,22 @@ FwdShape fwd_shape(int B, int H, int N, int compute_units) {
     s.split = true;
     s.qblocks = (N + 31) / 32;  // N <= 256 here
   } else {
-    // Otherwise the largest workgroup (more K/V reuse per LDS tile) that
-    // still gives at least two workgroups per compute unit on the 256-CU
-    // part.
+    // Otherwise the largest workgroup that still gives a workgroup to at
+    // least half the compute units (128 when their count is unknown).
+    // Every workgroup holds a whole LDS ring, so two fit on a compute unit
+    // whatever their size: four waves share each fetched K/V tile four
+    // ways, and two or one leave a compute unit with four or two waves to
+    // hide latency with.  On 256 compute units (A/B, us per call, against
+    // the earlier rule of at least 512 workgroups): 384 px x 2, 4 and 5
+    // images 14.1, 21.5 and 23.5 against 25.8, 28.2 and 30.0; ViT-L/14 at
+    // 4, 6, 8 and 10 images 7.9, 10.4, 10.6 and 10.9 against 13.6, 14.4,
+    // 15.0 and 15.4; one image at N = 1025 15.9 against 29.6.  Below half,
+    // more and smaller workgroups spread the latency better.
+    const int64_t min_wgs = compute_units > 0 ? compute_units / 2 : 128;
     s.waves = 1;
     for (int nw = 4; nw > 1; nw >>= 1) {
       const int64_t qb = (static_cast<int64_t>(N) + 32 * nw - 1) / (32 * nw);
-      if (pairs * qb >= 512) {
+      if (pairs * qb >= min_wgs) {
         s.waves = nw;
         break;
       }
