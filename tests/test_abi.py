@@ -348,7 +348,9 @@ def test_fwd_shape_describes_the_launch_without_a_device(va):
         (4, 16, 729, 72): (4, False, 64 * 6),
         (6, 16, 729, 72): (4, False, 96 * 6),
         (48, 16, 729, 72): (4, False, 768 * 6),
-        (64, 16, 256, 72): (4, False, 1024 * 2),  # 2048 blocks of 32: not split
+        (64, 16, 256, 72): (4, False, 1024 * 2),  # items of 128 fill the chip: not split
+        (8, 16, 256, 72): (4, False, 128 * 2),    # 256 items of 128, one per compute unit
+        (4, 16, 256, 72): (4, True, 64 * 8),      # 128 items of 128 would leave half idle
     }
     for (B, H, N, D), (waves, split, items) in cases.items():
         got = va.fwd_shape(B, H, N, D)

@@ -85,8 +85,8 @@ def test_stress_logits_parity(dev, va, N, D):
                                    (8, 16, 256), (12, 16, 200), (6, 16, 729)])
 def test_grid_shapes(dev, va, B, H, N):
     """Grids with every wave count the launcher picks, and uneven XCD splits.
-    (8, 16, 256) and (12, 16, 200) are split-key grids of 1024 and 1344
-    workgroups, several per compute unit; (6, 16, 729), one GPU's share of
+    (8, 16, 256) and (12, 16, 200) are short sequences on 256 and 384
+    four-wave workgroups; (6, 16, 729), one GPU's share of
     48 images at 384 px over 8 GPUs, gives 576 items on the 512 looping
     workgroups that fit on the chip at once, 64 of them taking a second."""
     wl = Workload("t", "grid", B=B, N=N, H=H, D=72, layout=LAYOUT_PACKED, layers=1, kind="iid",

@@ -35,10 +35,13 @@ PATHS = [
     # split keys, D = 72: SigLIP at 224 px x 2 (4 key tiles)
     ("split72_siglip224x2", 2, 16, 256, 72, LAYOUT_PACKED, "gamma", (4, True, False)),
     # split keys with many heads and several images: the first item's
-    # coordinates come from multiply-shift divisions by qblocks and H (2040
-    # and 1530 items, H not a power of two)
-    ("split64_170heads_x3", 3, 170, 100, 64, LAYOUT_SEPARATE, "iid", (4, True, False)),
-    ("split72_255heads_x2", 2, 255, 96, 72, LAYOUT_PACKED, "gamma", (4, True, False)),
+    # coordinates come from multiply-shift divisions by qblocks and H (1016
+    # and 747 items, H not a power of two)
+    ("split64_127heads_x2", 2, 127, 100, 64, LAYOUT_SEPARATE, "iid", (4, True, False)),
+    ("split72_83heads_x3", 3, 83, 96, 72, LAYOUT_PACKED, "gamma", (4, True, False)),
+    # short sequences whose 128-query items give every compute unit a
+    # workgroup: four waves per item, not split (8 images at N = 256)
+    ("nw4_one_n256x8", 8, 16, 256, 72, LAYOUT_PACKED, "gamma", (4, False, False)),
     # one wave per workgroup: ViT-B/16 at 384 px, one image (12 heads, 19
     # query blocks: 228 items; two waves would give 120 workgroups)
     ("nw1_vitb384x1", 1, 12, 577, 64, LAYOUT_PACKED, "iid", (1, False, False)),

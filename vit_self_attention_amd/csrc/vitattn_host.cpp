@@ -168,17 +168,24 @@ FwdShape fwd_shape(int B, int H, int N, int compute_units) {
   FwdShape s{};
   const int64_t pairs = static_cast<int64_t>(B) * H;
   const int64_t ntiles = (static_cast<int64_t>(N) + 63) / 64;
-  // Short sequences (2..4 key tiles of 64) on grids too small to fill the
-  // chip: the four waves of a workgroup split the keys of one 32-query
-  // block.  (Fewer than 2048 items: the kernel's coordinate arithmetic for
-  // this path is exact only below that count.)
-  if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 31) / 32) < 2048) {
+  // (256, the MI355X's count, when the device is unknown)
+  const int64_t cus = compute_units > 0 ? compute_units : 256;
+  // Short sequences (2..4 key tiles of 64) on grids where four-wave
+  // workgroups of 128 queries would not give every compute unit one: the
+  // four waves of a workgroup split the keys of one 32-query block
+  // instead, four times the workgroups.  With a workgroup per compute
+  // unit or more, the 128-query items win (8 images at N = 256: 9.2
+  // against 10.2 us, 12 at N = 200: 11.8 against 13.4; below, 4 images at
+  // N = 256: 6.0 split against 8.5).  (Fewer than 2048 items: the
+  // kernel's coordinate arithmetic for this path is exact only below that
+  // count.)
+  if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 127) / 128) < cus && pairs * ((N + 31) / 32) < 2048) {
     s.waves = 4;
     s.split = true;
     s.qblocks = (N + 31) / 32;  // N <= 256 here
   } else {
     // Otherwise the largest workgroup that still gives a workgroup to at
-    // least half the compute units (128 when their count is unknown).
+    // least half the compute units.
     // Every workgroup holds a whole LDS ring, so two fit on a compute unit
     // whatever their size: four waves share each fetched K/V tile four
     // ways, and two or one leave a compute unit with four or two waves to
@@ -188,7 +195,7 @@ FwdShape fwd_shape(int B, int H, int N, int compute_units) {
     // 4, 6, 8 and 10 images 7.9, 10.4, 10.6 and 10.9 against 13.6, 14.4,
     // 15.0 and 15.4; one image at N = 1025 15.9 against 29.6.  Below half,
     // more and smaller workgroups spread the latency better.
-    const int64_t min_wgs = compute_units > 0 ? compute_units / 2 : 128;
+    const int64_t min_wgs = cus / 2;
     s.waves = 1;
     for (int nw = 4; nw > 1; nw >>= 1) {
       const int64_t qb = (static_cast<int64_t>(N) + 32 * nw - 1) / (32 * nw);
