@@ -330,20 +330,22 @@ def test_linear_empty_is_a_noop(va):
 
 def test_fwd_shape_describes_the_launch_without_a_device(va):
     """vitattn_fwd_shape on the CPU (no device: the compute-unit count is
-    unknown, so no workgroup loops): the split-key choice for short
-    sequences on small grids, and the largest wave count that still gives
-    128 workgroups (half the compute units of the 256-CU part; the count
-    assumed when there is no device)."""
+    unknown, so no workgroup loops; 256 compute units are assumed): the
+    split-key choice on grids that four-wave items would leave
+    underfilled, and otherwise the largest wave count that still gives 128
+    workgroups (half the compute units)."""
     cases = {
         # (B, H, N, D): (waves, split_keys, items)
         (1, 12, 197, 64): (4, True, 12 * 7),     # 4 key tiles, 84 blocks of 32 queries
         (3, 12, 101, 64): (4, True, 36 * 4),     # 2 key tiles
         (2, 16, 256, 72): (4, True, 32 * 8),     # 4 key tiles
         (1, 1, 64, 72): (1, False, 2),           # one key tile: never split
-        (1, 1, 729, 72): (1, False, 23),         # 12 key tiles, tiny grid
-        (1, 12, 577, 64): (1, False, 12 * 19),   # 2 waves would give 120 < 128 workgroups
-        (2, 16, 257, 64): (2, False, 32 * 5),    # 4 waves would give 96 < 128 workgroups
-        (1, 16, 729, 72): (2, False, 16 * 12),
+        (1, 1, 729, 72): (4, True, 23),          # 12 key tiles, tiny grid: split, 3 tiles a wave
+        (1, 12, 577, 64): (4, True, 12 * 19),    # 4 waves would give 60 < 128 workgroups
+        (2, 16, 257, 64): (4, True, 32 * 9),     # 5 key tiles, 96 four-wave items
+        (1, 16, 729, 72): (4, True, 16 * 23),
+        (1, 1, 8192, 64): (2, False, 128),       # 256 blocks of 32: past the split's bounds
+        (1, 4, 64, 64): (1, False, 4 * 2),       # one key tile: never split
         (8, 16, 257, 64): (4, False, 128 * 3),
         (4, 16, 729, 72): (4, False, 64 * 6),
         (6, 16, 729, 72): (4, False, 96 * 6),

@@ -42,19 +42,23 @@ PATHS = [
     # short sequences whose 128-query items give every compute unit a
     # workgroup: four waves per item, not split (8 images at N = 256)
     ("nw4_one_n256x8", 8, 16, 256, 72, LAYOUT_PACKED, "gamma", (4, False, False)),
-    # one wave per workgroup: ViT-B/16 at 384 px, one image (12 heads, 19
-    # query blocks: 228 items; two waves would give 120 workgroups)
-    ("nw1_vitb384x1", 1, 12, 577, 64, LAYOUT_PACKED, "iid", (1, False, False)),
-    # one wave per workgroup (a single image and head: 23 items)
-    ("nw1_d64", 1, 1, 729, 64, LAYOUT_PACKED, "stress", (1, False, False)),
-    ("nw1_d72", 1, 1, 729, 72, LAYOUT_PACKED, "stress", (1, False, False)),
-    # two waves per workgroup: ViT-L/14 at 224 px, two views (160 items;
-    # four waves would give 96 workgroups)
-    ("nw2_vitl224x2", 2, 16, 257, 64, LAYOUT_PACKED, "iid", (2, False, False)),
-    ("nw2_vitl224x2_d72", 2, 16, 257, 72, LAYOUT_PACKED, "iid", (2, False, False)),
-    # two waves per workgroup: 384 px, one image (192 items)
-    ("nw2_384x1_d64", 1, 16, 729, 64, LAYOUT_PACKED, "stress", (2, False, False)),
-    ("nw2_384x1_d72", 1, 16, 729, 72, LAYOUT_PACKED, "stress", (2, False, False)),
+    # split keys over more than 4 key tiles, each wave taking tiles w,
+    # w + 4, ...: ViT-B/16 at 384 px, one image (10 tiles, 228 items); one
+    # head at N = 729 (12 tiles, 23 items); ViT-L/14 at 224 px, two views
+    # (5 tiles: wave 0 takes two); SigLIP at 384 px, one image (368 items)
+    ("msplit_vitb384x1", 1, 12, 577, 64, LAYOUT_PACKED, "iid", (4, True, False)),
+    ("msplit_1head_n729_d64", 1, 1, 729, 64, LAYOUT_PACKED, "stress", (4, True, False)),
+    ("msplit_1head_n729_d72", 1, 1, 729, 72, LAYOUT_PACKED, "stress", (4, True, False)),
+    ("msplit_vitl224x2", 2, 16, 257, 64, LAYOUT_PACKED, "iid", (4, True, False)),
+    ("msplit_vitl224x2_d72", 2, 16, 257, 72, LAYOUT_SEPARATE, "iid", (4, True, False)),
+    ("msplit_384x1_d72", 1, 16, 729, 72, LAYOUT_PACKED, "stress", (4, True, False)),
+    # one wave per workgroup: one key tile (N = 64), four heads (8 items)
+    ("nw1_n64_d64", 1, 4, 64, 64, LAYOUT_PACKED, "stress", (1, False, False)),
+    ("nw1_n64_d72", 1, 4, 64, 72, LAYOUT_SEPARATE, "stress", (1, False, False)),
+    # two waves per workgroup: one head at N = 8192 (256 blocks of 32, past
+    # the split's bounds; 128 items)
+    ("nw2_n8192_d64", 1, 1, 8192, 64, LAYOUT_PACKED, "stress", (2, False, False)),
+    ("nw2_n8192_d72", 1, 1, 8192, 72, LAYOUT_PACKED, "stress", (2, False, False)),
     # four waves, one workgroup per item, fewer workgroups than slots:
     # ViT-L/14 at 224 px x 8 and 384 px x 4 (384 items each)
     ("nw4_one_vitl224x8", 8, 16, 257, 64, LAYOUT_PACKED, "iid", (4, False, False)),

@@ -14,10 +14,10 @@
 //     more items than four-wave workgroup slots, two four-wave workgroups
 //     per compute unit loop over the items instead, fetching the next
 //     item's tiles while they finish the current one;
-//   * short sequences (2..4 key tiles) on small grids split the keys
-//     instead (kSplit): the four waves share one 32-query block, each
-//     reduces one key tile on its own, and the partial results merge
-//     through LDS;
+//   * small grids split the keys instead (kSplit): the four waves share
+//     one 32-query block, each reduces key tiles w, w+4, ... on its own
+//     (more than one with kMulti, for more than 4 key tiles), and the
+//     partial results merge through LDS;
 //   * keys in tiles of 64, fetched cooperatively with 128-bit direct-to-LDS
 //     loads into a ring of LDS stages (row-major K and V), three tiles ahead
 //     of the tile being reduced, one barrier per tile;
@@ -251,12 +251,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return x * q + (x < r ? x : r) + i;
 }
 
-// kSplit (short sequences, at most kStages key tiles, NW = 4): the waves of
-// a workgroup share one block of 32 queries, wave w fetches and reduces key
-// tile w on its own, and the partial results are merged through LDS at the
-// end.  This gives four times the waves for grids too small to fill the
-// chip.
-template <int D, int NW, bool kSplit, bool kF16>
+// kSplit (NW = 4): the waves of a workgroup share one block of 32 queries,
+// wave w fetches and reduces key tile w on its own (and, with kMulti, tiles
+// w + 4, w + 8, ... after it, in the same LDS stage), and the partial
+// results are merged through LDS at the end.  This gives four times the
+// waves for grids too small to fill the chip.
+template <int D, int NW, bool kSplit, bool kF16, bool kMulti = false>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int H, int N_, int i_st,
                                                       float cs, const uint16_t* q, const uint16_t* k,
                                                       const uint16_t* v, uint16_t* o, int items) {
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
           if (i + 2 == kHalfPv) {
             wait_vmcnt<0>();
             asm volatile("" ::: "memory");
-            if (half == 1) write_ones(gs);
+            if (half == 1) write_ones(stage_of(gs));
           }
         }
         if (i + 2 < kPv) vo[i + 2] = v_read(vt, i + 2);
@@ -899,10 +899,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     // flight.
     const int my = wave;
     if (wave_active && my < ntiles) {
-      const int kb0 = my * kBlockN;
       const uint32_t stage = lds_base + 2 * my * kStageElems;
-      // fetch instructions [lo, hi) of tile my (I < kKInstr fill K slots)
-      auto fetch_own = [&](int lo, int hi) __attribute__((always_inline)) {
+      // fetch instructions [lo, hi) of tile t (I < kKInstr fill K slots)
+      auto fetch_own = [&](int t, int lo, int hi) __attribute__((always_inline)) {
+        const int kb0 = t * kBlockN;
         const char* gk = reinterpret_cast<const char*>(kbase + static_cast<int64_t>(kb0) * a.i_st);
         const char* gv = reinterpret_cast<const char*>(vbase + static_cast<int64_t>(kb0) * a.i_st);
         const int last = N - 1 - kb0;
@@ -931,7 +931,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
           dma16(gq, static_cast<uint32_t>((row * st32 + cc * 8) * 2), stage + 2 * (kKTile + i * 512));
         }
       }
-      fetch_own(0, kKInstr);
+      fetch_own(my, 0, kKInstr);
       wait_vmcnt<kKInstr>();  // the query rows landed
       asm volatile("" ::: "memory");
       {
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the V rows land on them
       sign_q(qf, qt);
-      fetch_own(kKInstr, kInstr);
+      fetch_own(my, kKInstr, kInstr);
       // K rows 0..35 (the first five fetches) carry key block 0, the rest
       // block 1; V rows 0..31 (the first five) keys 0..31 of P V
       constexpr int kHalfFetch = 5;
@@ -961,6 +961,28 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       if (half == 0) write_ones(my);  // rows 0..31 (lane = row); rows 32..63 in the step
       if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{}, False{}, False{});
       else step(my, my, sa, sb, False{}, False{}, False{}, False{});
+      if constexpr (kMulti) {
+        // the wave's further tiles my + 4, my + 8, ... in the same stage
+        // (tile t lives in stage t % 4 = wave), one after another: K, then
+        // V, with Q K^T of each 32-key block as soon as its K rows land
+        for (int t = my + 4; t < ntiles; t += 4) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the last tile's reads returned
+          fetch_own(t, 0, kInstr);
+          wait_vmcnt<kVInstr + kKInstr - kHalfFetch>();
+          asm volatile("" ::: "memory");
+          qk_block(lds + my * kStageElems, sa, 0);
+          wait_vmcnt<kVInstr>();
+          asm volatile("" ::: "memory");
+          qk_block(lds + my * kStageElems, sa, 1);
+          mx = rowmax(sa);
+          asm volatile("" ::"v"(mx));
+          wait_vmcnt<kVInstr - kHalfFetch>();
+          asm volatile("" ::: "memory");
+          if (half == 0) write_ones(my);
+          if (ragged && t == ntiles - 1) step(t, t, sa, sb, False{}, True{}, False{}, False{});
+          else step(t, t, sa, sb, False{}, False{}, False{}, False{});
+        }
+      }
     }
     // ---- merge the partial results of the waves (each: running max m,
     // accumulator, and for D = 64 the partial row sum) through LDS.  Wave w
@@ -1137,14 +1159,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   }
 }
 
-template <int D, int NW, bool kSplit, bool kF16>
+template <int D, int NW, bool kSplit, bool kF16, bool kMulti = false>
 int launch(const KernelArgs& ka, hipStream_t stream) {
   int qblocks = ka.qblocks, H = ka.H;
   if constexpr (kSplit) {
     // the split kernel divides by qblocks and H with multipliers packed
     // above them: exact while items * qblocks <= 2^16 and pairs * H <= 2^20,
     // and the products item * mq and pair * mh must fit in 32 bits (the
-    // split path has fewer than 2048 items and at most 8 query blocks)
+    // launcher picks the split path only within these bounds)
     if (ka.qblocks < 1 || ka.qblocks > 255 || H < 1 || H > 2047) return VITATTN_ERR_LAUNCH;
     const int64_t pairs = ka.items / ka.qblocks;
     const int64_t mq = ((int64_t(1) << 16) + ka.qblocks - 1) / ka.qblocks;
@@ -1155,7 +1177,7 @@ int launch(const KernelArgs& ka, hipStream_t stream) {
     qblocks = static_cast<int>(static_cast<uint32_t>(ka.qblocks) | (static_cast<uint32_t>(mq) << 8));
     H = static_cast<int>(static_cast<uint32_t>(H) | (static_cast<uint32_t>(mh) << 11));
   }
-  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit, kF16>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka.grid,
+  hipLaunchKernelGGL((fwd_kernel<D, NW, kSplit, kF16, kMulti>), dim3(ka.grid), dim3(64 * NW), 0, stream, ka.grid,
                      qblocks, H, ka.N, ka.i_st, ka.qsign ? -ka.c : ka.c, ka.q, ka.k, ka.v, ka.o, ka.items);
   return hipGetLastError() == hipSuccess ? VITATTN_OK : VITATTN_ERR_LAUNCH;
 }
@@ -1181,13 +1203,15 @@ namespace {
 
 template <bool kF16>
 int launch_typed(const KernelArgs& ka, int D, const FwdShape& sh, hipStream_t s) {
+  // split keys over more than 4 key tiles: waves loop over their tiles
+  const bool multi = ka.N > 4 * kBlockN;
   if (D == 64) {
-    if (sh.split) return launch<64, 4, true, kF16>(ka, s);
+    if (sh.split) return multi ? launch<64, 4, true, kF16, true>(ka, s) : launch<64, 4, true, kF16>(ka, s);
     if (sh.waves == 4) return launch<64, 4, false, kF16>(ka, s);
     if (sh.waves == 2) return launch<64, 2, false, kF16>(ka, s);
     return launch<64, 1, false, kF16>(ka, s);
   }
-  if (sh.split) return launch<72, 4, true, kF16>(ka, s);
+  if (sh.split) return multi ? launch<72, 4, true, kF16, true>(ka, s) : launch<72, 4, true, kF16>(ka, s);
   if (sh.waves == 4) return launch<72, 4, false, kF16>(ka, s);
   if (sh.waves == 2) return launch<72, 2, false, kF16>(ka, s);
   return launch<72, 1, false, kF16>(ka, s);

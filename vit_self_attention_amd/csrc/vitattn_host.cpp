@@ -170,19 +170,26 @@ FwdShape fwd_shape(int B, int H, int N, int compute_units) {
   const int64_t ntiles = (static_cast<int64_t>(N) + 63) / 64;
   // (256, the MI355X's count, when the device is unknown)
   const int64_t cus = compute_units > 0 ? compute_units : 256;
-  // Short sequences (2..4 key tiles of 64) on grids where four-wave
-  // workgroups of 128 queries would not give every compute unit one: the
-  // four waves of a workgroup split the keys of one 32-query block
-  // instead, four times the workgroups.  With a workgroup per compute
-  // unit or more, the 128-query items win (8 images at N = 256: 9.2
-  // against 10.2 us, 12 at N = 200: 11.8 against 13.4; below, 4 images at
-  // N = 256: 6.0 split against 8.5).  (Fewer than 2048 items: the
-  // kernel's coordinate arithmetic for this path is exact only below that
-  // count.)
-  if (ntiles >= 2 && ntiles <= 4 && pairs * ((N + 127) / 128) < cus && pairs * ((N + 31) / 32) < 2048) {
+  // Split keys: the four waves of a workgroup share one 32-query block and
+  // take its key tiles in turn (w, w + 4, ...), for four times the
+  // workgroups of 128-query items.  For short sequences (2..4 key tiles)
+  // while those items would not give every compute unit one: with a
+  // workgroup per compute unit or more the 128-query items win (8 images
+  // at N = 256: 9.2 against 10.2 us split; 12 at N = 200: 11.8 against
+  // 13.4; below, 4 images at N = 256: 6.0 split against 8.5).  For longer
+  // ones while four-wave items would not reach half the compute units
+  // (where one- and two-wave workgroups ran before: SigLIP 384 px, one
+  // image, 10.4 against 13.1 us; ViT-B/16 384 px, one image, 6.1 against
+  // 10.2; one head at N = 2048, 11.4 against 24.7).  Within the bounds of
+  // the kernel's multiply-shift coordinate arithmetic (fewer than 2048
+  // items, items * qblocks <= 2^16, pairs * H <= 2^20).
+  const int64_t qb32 = (static_cast<int64_t>(N) + 31) / 32, qb128 = (static_cast<int64_t>(N) + 127) / 128;
+  const bool div_ok = qb32 <= 255 && H <= 2047 && pairs * qb32 < 2048 &&
+                      pairs * qb32 * qb32 <= (int64_t(1) << 16) && pairs * H <= (int64_t(1) << 20);
+  if (ntiles >= 2 && div_ok && (ntiles <= 4 ? pairs * qb128 < cus : pairs * qb128 < cus / 2)) {
     s.waves = 4;
     s.split = true;
-    s.qblocks = (N + 31) / 32;  // N <= 256 here
+    s.qblocks = static_cast<int>(qb32);
   } else {
     // Otherwise the largest workgroup that still gives a workgroup to at
     // least half the compute units.
