@@ -680,6 +680,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   float m_run = -__builtin_inff();
   float l_run = 0.f;  // per-lane partial row sum (D = 64)
 
+  // (split kernel with kMulti: the K rows of the wave's next tile are in
+  // flight behind this tile's V rows)
+  bool pend_k = false;
   // ---- one key tile j.  `cur` holds the logits of tile j; when kNext,
   // the logits of tile j+1 go to `nxt` and their row max to mx.  kRagged
   // (last tile, N not a multiple of 64) zeroes the weights of keys >= N.
@@ -808,7 +811,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
           // the split kernel enters with V rows 0..31 landed; rows 32..63
           // (keys of steps t = 2, 3) are waited for before their first read
           if (i + 2 == kHalfPv) {
-            wait_vmcnt<0>();
+            if constexpr (kMulti) {
+              if (pend_k) wait_vmcnt<kKInstr>();
+              else wait_vmcnt<0>();
+            } else {
+              wait_vmcnt<0>();
+            }
             asm volatile("" ::: "memory");
             if (half == 1) write_ones(stage_of(gs));
           }
@@ -956,8 +964,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       qk_block(lds + my * kStageElems, sa, 1);
       mx = rowmax(sa);
       asm volatile("" ::"v"(mx));  // the row max is taken before the wait below
-      wait_vmcnt<kVInstr - kHalfFetch>();  // V rows 0..31 landed
-      asm volatile("" ::: "memory");
+      // (kMulti) the next tile's K rows go out now, into the K region this
+      // tile's Q K^T has finished reading, and land during its P V
+      auto fetch_next_k = [&](int t) __attribute__((always_inline)) {
+        if constexpr (kMulti) {
+          pend_k = t + 4 < ntiles;
+          if (pend_k) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            fetch_own(t + 4, 0, kKInstr);
+          }
+        }
+      };
+      auto wait_v_half = [&]() __attribute__((always_inline)) {
+        if (pend_k) wait_vmcnt<kVInstr - kHalfFetch + kKInstr>();
+        else wait_vmcnt<kVInstr - kHalfFetch>();  // V rows 0..31 landed
+        asm volatile("" ::: "memory");
+      };
+      fetch_next_k(my);
+      wait_v_half();
       if (half == 0) write_ones(my);  // rows 0..31 (lane = row); rows 32..63 in the step
       if (ragged && my == ntiles - 1) step(my, my, sa, sb, False{}, True{}, False{}, False{});
       else step(my, my, sa, sb, False{}, False{}, False{}, False{});
@@ -965,9 +989,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
         // the wave's further tiles my + 4, my + 8, ... in the same stage
         // (tile t lives in stage t % 4 = wave), one after another: K, then
         // V, with Q K^T of each 32-key block as soon as its K rows land
-        for (int t = my + 4; t < ntiles; t += 4) {
+        // the V rows of tile my + 4 follow its K rows, after this tile's P V
+        if (pend_k) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the last tile's reads returned
-          fetch_own(t, 0, kInstr);
+          fetch_own(my + 4, kKInstr, kInstr);
+        }
+        for (int t = my + 4; t < ntiles; t += 4) {
           wait_vmcnt<kVInstr + kKInstr - kHalfFetch>();
           asm volatile("" ::: "memory");
           qk_block(lds + my * kStageElems, sa, 0);
@@ -976,11 +1003,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
           qk_block(lds + my * kStageElems, sa, 1);
           mx = rowmax(sa);
           asm volatile("" ::"v"(mx));
-          wait_vmcnt<kVInstr - kHalfFetch>();
-          asm volatile("" ::: "memory");
+          fetch_next_k(t);
+          wait_v_half();
           if (half == 0) write_ones(my);
           if (ragged && t == ntiles - 1) step(t, t, sa, sb, False{}, True{}, False{}, False{});
           else step(t, t, sa, sb, False{}, False{}, False{}, False{});
+          if (pend_k) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            fetch_own(t + 4, kKInstr, kInstr);
+          }
         }
       }
     }
