@@ -320,7 +320,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   constexpr int kMinPerWave = kInstr / NW;           // ... and of the least busy one
   static_assert(kBlockN * kKSlotsRow % 64 == 0 && kBlockN * kVSlotsRow % 64 == 0, "slots");
 
-  // the ring, then a 1 KB sink that touch_q's fetches land in (never read)
+  // the ring, then a 1 KB sink for the filler fetches of waves with fewer
+  // fetch instructions in a steady step (never read)
   constexpr int kSinkElems = 512;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStageElems + kSinkElems];
   // byte address of lds in the LDS aperture (what M0 takes)
@@ -445,19 +446,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
     sign_q(qf, qt);
   }
   int nb = b, nh = h, nqb = qb;  // next item (the current one after the last)
-  // Brings the next item's query rows of this wave into the caches, ahead
-  // of load_q: one direct-to-LDS fetch of each row's
-  // first and last 16-byte chunks (every cache line a row of 2*D <= 144
-  // bytes touches), landing in the LDS sink.
-  auto touch_q = [&]() __attribute__((always_inline)) {
-    const int qn0 = first_query(nqb);
-    const int qlo = qn0 < N ? qn0 : N - 1;
-    const int r = qn0 + col < N ? qn0 + col : N - 1;
-    const char* base = reinterpret_cast<const char*>(a.q + nb * a.i_sb + nh * a.i_sh +
-                                                     static_cast<int64_t>(qlo) * a.i_st);
-    const uint32_t off = static_cast<uint32_t>((r - qlo) * a.i_st * 2 + (2 * D - 16) * half);
-    dma16(base, off, lds_base + 2 * kStages * kStageElems);
-  };
 
   // ---- direct-to-LDS tile fetch.  Fetch instruction i of this wave is
   // number I = i*NW + wave of the tile: I < kKInstr fills K slots, the rest
@@ -570,20 +558,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   };
   // Waits until the fetches of all but the last `tiles_in_flight` (0 or 1)
   // tiles issued by this wave have landed (vector-memory counter only; a
-  // wave issues at least kMinPerWave fetches per tile, and kLater other
-  // loads after them), then meets the rest of the workgroup.  The memory
-  // clobber keeps LDS accesses after it.
-  auto wait_fetch_and_sync = [&](int tiles_in_flight, auto kLaterC) __attribute__((always_inline)) {
-    constexpr int kLater = decltype(kLaterC)::value;
-    asm volatile("" ::: "memory");  // the later loads stay ahead of the count
+  // wave issues at least kMinPerWave fetches per tile, and no other load
+  // after them), then meets the rest of the workgroup.  The memory clobber
+  // keeps LDS accesses after it.
+  auto wait_fetch_and_sync = [&](int tiles_in_flight) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
     if (tiles_in_flight == 0) {
-      wait_vmcnt<kLater>();
+      wait_vmcnt<0>();
     } else {
-      wait_vmcnt<kMinPerWave + kLater>();
+      wait_vmcnt<kMinPerWave>();
     }
     asm volatile("s_barrier" ::: "memory");
   };
-  using NoLater = std::integral_constant<int, 0>;
   // tiles fetched after tile t (0 or 1 with a four-stage ring), at the point
   // where the fetch of tile `issued` is the last one
   auto after = [&](int t, int issued) { return issued > t ? issued - t : 0; };
@@ -714,10 +700,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       // stage (gs-1) % kStages held stream tile gs-1, whose reads all ended
       // before the last barrier; it is refilled with stream tile gs + kStages - 1
       fetch_next();
-      // three steps before the item ends: touch the next item's query rows.
-      // Issued after this step's fetches, it has two steps to land: the
-      // wait at the end of this step leaves it in flight, the next one not.
-      if (kNext && j == ntiles - 3 && gs + 3 < stream_len) touch_q();
       // stream tile gs+1 landed before the last barrier; its V is read next step
       if (gs + 1 < stream_len) write_ones(stage_of(gs + 1));
     }
@@ -874,18 +856,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
       asm volatile("s_barrier" ::: "memory");
     } else if constexpr (!kSplit) {
       if constexpr (kNext) {
-        if (j == ntiles - 3 && gs + 3 < stream_len) {
-          wait_fetch_and_sync(after(gs + 2, f_s - 1), std::integral_constant<int, 1>{});
-        } else if (gs + 1 < stream_len) {
-          wait_fetch_and_sync(after(gs + 2, f_s - 1), NoLater{});
-        }
+        if (gs + 1 < stream_len) wait_fetch_and_sync(after(gs + 2, f_s - 1));
       } else {
         // Everything this wave has in flight, the next item's query rows
         // included, lands here (its last fetch was issued a step ago): the
         // compiler's own waits for those rows then find nothing left to wait
         // for in the next item, where a count of its loads alone would also
         // wait for fetches issued after them.
-        wait_fetch_and_sync(0, NoLater{});
+        wait_fetch_and_sync(0);
       }
     }
   };
@@ -1087,7 +1065,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
   // are zeroed.
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t) fetch_next();
-  wait_fetch_and_sync(after(1, f_s - 1), NoLater{});
+  wait_fetch_and_sync(after(1, f_s - 1));
   write_ones(0);
 
   int g0 = 0;  // stream index of the current item's tile 0
