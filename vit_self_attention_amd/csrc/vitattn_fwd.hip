@@ -1148,11 +1148,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
             }
           }
         // store k covers rows kRows*k .. kRows*k + kRows-1: lane l writes
-        // 16-byte chunk l % (D/8) of row kRows*k + l / (D/8).  The stores are
-        // non-temporal: nothing in the kernel reads the output again, and
-        // kept out of the way it leaves the L2 to the K and V tiles that the
-        // other query blocks of the same (image, head) still read (384 px:
-        // 182 against 191 us; ViT-L/14 224 px x 24: 22.8 against 23.8).
+        // 16-byte chunk l % (D/8) of row kRows*k + l / (D/8).  Ordinary
+        // (write-back) stores: the next kernel of an encoder block, the output
+        // projection, reads this output at once and finds it in the caches.
+        // Non-temporal stores made this call about 4% faster on its own but
+        // the projection after it slower by more (384 px: the pair took 328
+        // against 316 us).
         constexpr int kRowChunks = D / 8, kRows = 64 / kRowChunks;
         const int r0 = lane / kRowChunks, ch = lane - r0 * kRowChunks;
         const uint16_t* src = ob + r0 * kOS + 8 * ch;
@@ -1162,8 +1163,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(int grid, int qblocks, int
         for (int k = 0; k < (32 + kRows - 1) / kRows; ++k) {
           const int row = kRows * k + r0;
           if (r0 < kRows && row < 32 && q0 + row < N)
-            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src + kRows * k * kOS),
-                                        reinterpret_cast<u32x4*>(dst));
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src + kRows * k * kOS);
           dst += dst_step;
         }
       }

@@ -113,7 +113,8 @@ __device__ __forceinline__ int lxcd_remap(int bid, int grid) {
   return x * q + (x < r ? x : r) + i;
 }
 
-template <int WM, int WN, int TM, int TN, bool kF16>
+// kStream: the output goes out with non-temporal stores (see launch_linear_typed)
+template <int WM, int WN, int TM, int TN, bool kF16, bool kStream>
 __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
   constexpr int NW = WM * WN;
   constexpr int BM = WM * TM, BN = WN * TN;
@@ -324,23 +325,23 @@ __global__ __launch_bounds__(64 * WM * WN) void linear_kernel(LinearArgs a) {
       w.y = pack16x2<kF16>(v[2], v[3]);
       w.z = pack16x2<kF16>(v[4], v[5]);
       w.w = pack16x2<kF16>(v[6], v[7]);
-      // non-temporal: the output is not read again here, and streamed past
-      // the L2 it leaves that cache to the x and w rows other tiles still
-      // read (qkv projection at 384 px x 48: 322 against 330 us)
       const lu32x4 wv = {w.x, w.y, w.z, w.w};
-      __builtin_nontemporal_store(wv, reinterpret_cast<lu32x4*>(a.out + o));
+      if constexpr (kStream)
+        __builtin_nontemporal_store(wv, reinterpret_cast<lu32x4*>(a.out + o));
+      else
+        *reinterpret_cast<lu32x4*>(a.out + o) = wv;
     }
   }
 }
 
-template <int WM, int WN, int TM, int TN, bool kF16>
+template <int WM, int WN, int TM, int TN, bool kF16, bool kStream = false>
 int launch_linear_cfg(const LinearArgs& la0, hipStream_t s) {
   LinearArgs la = la0;
   constexpr int BM = WM * TM, BN = WN * TN;
   la.mblocks = (la.M + BM - 1) / BM;
   la.nblocks = (la.Nout + BN - 1) / BN;
   const int64_t grid = static_cast<int64_t>(la.mblocks) * la.nblocks;
-  hipLaunchKernelGGL((linear_kernel<WM, WN, TM, TN, kF16>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((linear_kernel<WM, WN, TM, TN, kF16, kStream>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WM * WN), 0, s, la);
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
@@ -357,7 +358,20 @@ int launch_linear_typed(const LinearArgs& la, hipStream_t s) {
   auto tiles = [&](int bm, int bn) {
     return static_cast<int64_t>((la.M + bm - 1) / bm) * ((la.Nout + bn - 1) / bn);
   };
-  if (tiles(256, 256) >= 256) return launch_linear_cfg<2, 4, 128, 64, kF16>(la, s);
+  if (tiles(256, 256) >= 256) {
+    // Outputs larger than half the 256 MB last-level cache go out with
+    // non-temporal stores: such an output cannot stay cached for the next
+    // kernel anyway, and streamed past the L2 it leaves that cache to the x
+    // and w rows other tiles still read (qkv projection at 384 px x 48,
+    // 242 MB: 322 against 330 us on its own, and with the attention call
+    // that reads it 481 against 487 us for the pair).  Smaller outputs use
+    // write-back stores, where the next kernel finds them (non-temporal
+    // stores gained nothing for the 80 MB output projection).  The smaller
+    // tiles below only serve outputs under 256 x 65536 elements.
+    if (static_cast<int64_t>(la.M) * la.Nout * 2 > (int64_t(128) << 20))
+      return launch_linear_cfg<2, 4, 128, 64, kF16, true>(la, s);
+    return launch_linear_cfg<2, 4, 128, 64, kF16>(la, s);
+  }
   if (tiles(128, 128) >= 256) return launch_linear_cfg<2, 2, 64, 64, kF16>(la, s);
   if (tiles(64, 64) <= 448) return launch_linear_cfg<2, 2, 32, 32, kF16>(la, s);
   return launch_linear_cfg<2, 2, 32, 64, kF16>(la, s);
