@@ -416,6 +416,96 @@ def _linear_figures(stream, steps=10, only=None):
     return res
 
 
+def _block_figure(stream, steps=10):
+    """The attention sublayer of a SigLIP-So400m block at 384 px x 48 as an
+    encoder runs it: the fused qkv projection (1152 -> 3456, bias) writes the
+    packed [B,N,3,H,D] buffer, the attention reads it, and the output
+    projection (1152 -> 1152, bias, residual = the block input) reads the
+    attention output.  Time per sublayer (median of 3 batches of `steps`
+    back-to-back sublayers between HIP events), each of the three calls
+    timed alone the same way for comparison, and sampled-row parity of every
+    stage with the fp64 oracle, each stage fed the previous stage's output."""
+    import numpy as np
+    import torch
+    import oracle
+    import vit_self_attention_amd as va
+    from oracle import linear as lo
+    from workloads import f32_to_bf16_bits
+
+    B, N, H, D = 48, 729, 16, 72
+    M, E = B * N, H * D
+    scale = D ** -0.5
+    rng = np.random.default_rng(23)
+    dev = torch.device("cuda:0")
+    x = f32_to_bf16_bits(rng.standard_normal((M, E)).astype(np.float32))
+    wq = f32_to_bf16_bits(rng.standard_normal((3 * E, E)).astype(np.float32) / np.float32(34.0))
+    bq = f32_to_bf16_bits(rng.standard_normal(3 * E).astype(np.float32) * np.float32(0.1))
+    wp = f32_to_bf16_bits(rng.standard_normal((E, E)).astype(np.float32) / np.float32(34.0))
+    bp = f32_to_bf16_bits(rng.standard_normal(E).astype(np.float32) * np.float32(0.1))
+
+    def dv(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xd, wqd, bqd, wpd, bpd = dv(x), dv(wq), dv(bq), dv(wp), dv(bp)
+    qkv = torch.empty((B, N, 3, H, D), dtype=torch.bfloat16, device=dev)
+    att = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, E), dtype=torch.bfloat16, device=dev)
+    calls = {
+        "qkv_projection": lambda: va.linear(xd, wqd, bqd, None, out=qkv.view(M, 3 * E), stream=stream),
+        "attention": lambda: va.fwd(qkv, None, None, scale=scale, out=att, stream=stream),
+        "output_projection": lambda: va.linear(att.view(M, E), wpd, bpd, xd, out=y, stream=stream),
+    }
+
+    def timed(fns):
+        for _ in range(5):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        batches = []
+        for _ in range(3):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(steps):
+                for f in fns:
+                    f()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            batches.append(t0.elapsed_time(t1) * 1e3 / steps)
+        return sorted(batches)[1], batches
+
+    alone = {k: timed([f])[0] for k, f in calls.items()}
+    us, batches = timed(list(calls.values()))
+    # parity of each stage on sampled rows, fed the previous stage's output
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 24)]))
+    qkv_bits = qkv.view(torch.int16).cpu().numpy().view(np.uint16)
+    att_bits = att.view(torch.int16).cpu().numpy().view(np.uint16)
+    e_q = np.abs(lo.widen(qkv_bits.reshape(M, 3 * E)[rows]) - lo.linear_rows(x, wq, bq, None, rows))
+    absq = np.abs(lo.widen(x[rows])) @ np.abs(lo.widen(wq)).T
+    trip = np.stack([rows // N, rng.integers(0, H, rows.size), rows % N], 1)
+    ref_a = oracle.attention_rows(qkv_bits, None, None, 1, B, H, N, D, scale, trip)
+    got_a = np.stack([lo.widen(att_bits[b, i, h]) for b, h, i in trip])
+    e_a = np.abs(got_a - ref_a)
+    e_p = np.abs(lo.widen(y.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+                 - lo.linear_rows(att_bits.reshape(M, E), wp, bp, x, rows))
+    absp = np.abs(lo.widen(att_bits.reshape(M, E)[rows])) @ np.abs(lo.widen(wp)).T
+    ok = (bool(np.all(e_q <= 2.0 ** -8 * np.abs(lo.linear_rows(x, wq, bq, None, rows)) + 2.0 ** -12 * absq))
+          and bool(e_a.max() <= 2e-2 and e_a.mean() <= 2e-3)
+          and bool(np.all(e_p <= 2.0 ** -8 * np.abs(lo.linear_rows(att_bits.reshape(M, E), wp, bp, x, rows))
+                          + 2.0 ** -12 * absp)))
+    flops = 2.0 * M * E * 3 * E + 4.0 * B * H * N * N * D + 2.0 * M * E * E
+    del xd, wqd, bqd, wpd, bpd, qkv, att, y
+    torch.cuda.empty_cache()
+    return {"workload": "SigLIP-So400m/14 384px, 3 views x batch 16 (B=48,N=729,H=16,D=72): "
+                        "qkv projection -> attention -> output projection with residual",
+            "us_per_sublayer": us, "batches_us_per_sublayer": batches,
+            "us_alone": alone, "sum_of_alone_us": sum(alone.values()),
+            "tflops": flops / (us * 1e-6) / 1e12,
+            "parity_pass": ok, "attention_sampled_rows_max_abs": float(e_a.max()),
+            "timing": "median of 3 batches of 10 back-to-back sublayers (and of each call alone), "
+                      "HIP events on the launch stream"}
+
+
 def _host_cpus():
     """CPUs this process may run on, and the share of them a job on this
     host is allotted (OMP_NUM_THREADS where the host sets it)."""
@@ -652,6 +742,9 @@ def main():
                       "events on the launch stream, after 100 warmup launches"}
         del tins, touts
 
+    if not args.no_target and FMT == "bf16":
+        result["attention_sublayer_384x48"] = _block_figure(stream)
+
     result["context_only"] = CONTEXT
     print(json.dumps(result), flush=True)
     failed = [name for name, p in (("parity", result.get("parity")),
@@ -659,6 +752,8 @@ def main():
                                     result.get("siglip384_target", {}).get("parity_sampled_rows")))
               if p is not None and not p["pass"]]
     failed += [f"linear.{k}" for k, v in result.get("linear", {}).items() if not v.get("parity_pass", True)]
+    if not result.get("attention_sublayer_384x48", {}).get("parity_pass", True):
+        failed.append("attention_sublayer_384x48")
     if failed:
         print(f"bench.py: parity check failed: {', '.join(failed)}", file=sys.stderr, flush=True)
         sys.exit(1)
