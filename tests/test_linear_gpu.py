@@ -104,6 +104,23 @@ def test_qkv_projection_siglip384_sampled_rows(dev, va):
     _check(out[rows], x, w, b, None, "bf16", rows=rows, what="qkv 384 sampled")
 
 
+@pytest.mark.parametrize("fmt,K,Nout,resid", [("f16", 1152, 3456, False), ("bf16", 64, 2048, True)])
+def test_streaming_store_path(dev, va, fmt, K, Nout, resid):
+    """Outputs above 128 MiB go out with non-temporal stores (a separate
+    kernel instantiation of the 256 x 256 tile shape): the fp16 qkv
+    projection at 384 px x 48, and a bf16 call with a residual (M = 34992,
+    Nout = 2048: 143 MB), on sampled rows."""
+    import torch
+    M = 48 * 729
+    assert M * Nout * 2 > 128 << 20
+    x, w, b, r = _inputs(40 + K, M, K, Nout, fmt, residual=resid)
+    out = va.linear(*[_dev(t, fmt, dev) for t in (x, w, b)], _dev(r, fmt, dev))
+    torch.cuda.synchronize(dev)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 40)]))
+    _check(_host(out)[rows], x, w, b, r, fmt, rows=rows, what=f"streaming {fmt} K={K} Nout={Nout}")
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
 def test_output_projection_with_residual(dev, va, fmt):
     """out = o w^T + b + x, with a separate output and in place (out is x)."""
